@@ -1,0 +1,191 @@
+"""PR-Sink hot-path benchmark on one MI355X.
+
+One step = one streamed block of the 480x480 workload (40 heads, d=128,
+Q=2700 tokens, K=14400 keys once the cache is full, 40 layers): pose
+retrieval + Dynamic Sink copy, 40 layers x 3 denoise-step attention calls,
+40 clean-KV writes, and the bank update (blocks < 20).  Inputs are synthetic,
+seeded and resident in HBM before the timed region; the attention inputs of a
+step cycle through pools of 7 distinct Q/K/V sets so consecutive calls do not
+reuse cached keys.
+
+Prints one JSON line.  `value` is attention TFLOP/s over the whole step (120
+attention calls' algorithmic FLOPs / block time); the attention kernel's own
+duration is taken with HIP events around every call on the library's stream.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "PR-Sink attn ms/call + TFLOP/s (% bf16 MFMA peak), 480×480 block; ms/block stream"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0
+POOL = 7                    # distinct input sets per pool (coprime to the layer count)
+
+
+def attn_flops(cfg) -> float:
+    return 4.0 * cfg.n_heads * cfg.block_tokens * cfg.full_cache_keys * cfg.head_dim
+
+
+def cpu_baseline(cfg, q, kc, vc, ref_kv_host, block_kv_host, orc, budget_s=12.0):
+    """The fp64 oracle on a bounded sample of the same attention call: whole heads
+    until ~budget_s of CPU time has been spent."""
+    import numpy as np
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count()
+    done, t_total = 0, 0.0
+    for h in range(cfg.n_heads):
+        t0 = time.perf_counter()
+        orc.attend(q, kc, vc, ref_kv_host, block_kv_host, heads=[h])
+        t_total += time.perf_counter() - t0
+        done += 1
+        if t_total >= budget_s:
+            break
+    flops = attn_flops(cfg) * done / cfg.n_heads
+    return {"value": round(flops / t_total / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{done} of {cfg.n_heads} heads of one 480x480 attention call "
+                      f"(Q=2700, K=14400, d=128), numpy fp64, {t_total:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--layers", type=int, default=40)
+    ap.add_argument("--seed", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: the PR-Sink path here runs on a single MI355X "
+              "(no collectives); run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from bounded_kv_cache_pr_amd import binding, build, synth
+
+    if not os.path.exists(build.LIB_PATH):
+        build.build_library()
+    dev = torch.device("cuda:0")
+    cfg = synth.C3_STREAM_480.replace(n_layers=args.layers)
+    L, steps = cfg.n_layers, synth.DENOISE_STEPS
+    n_blocks = args.warmup + args.steps
+    seed = args.seed
+
+    cache = binding.PRSinkCache(cfg, device=dev)
+    for l in range(L):
+        k, v = synth.ref_kv_torch(cfg, l, seed, dev)
+        cache.set_ref(l, k, v)
+    qkv_pool = [synth.step_qkv_torch(cfg, 10_000 + i, 0, 0, seed, dev) for i in range(POOL)]
+    clean_pool = [synth.clean_kv_torch(cfg, 20_000 + i, 0, seed, dev) for i in range(POOL)]
+    out = torch.empty_like(qkv_pool[0][0])
+    fps = torch.from_numpy(synth.pose_stream(n_blocks, seed=seed)).to(dev)
+    stream = torch.cuda.current_stream(dev)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps * L * args.steps)]
+
+    def run_block(b, timed_base=None):
+        cache.retrieve(b, fps[b])
+        for s in range(steps):
+            for l in range(L):
+                q, k, v = qkv_pool[(b * steps * L + s * L + l) % POOL]
+                if timed_base is not None:
+                    e0, e1 = ev[timed_base + s * L + l]
+                    e0.record(stream)
+                    cache.attend(l, q, k, v, out=out)
+                    e1.record(stream)
+                else:
+                    cache.attend(l, q, k, v, out=out)
+        for l in range(L):
+            k, v = clean_pool[(b * L + l) % POOL]
+            cache.clean_kv_write(l, k, v)
+        cache.bank_update(b)
+
+    for b in range(args.warmup):
+        run_block(b)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        run_block(args.warmup + i, timed_base=i * steps * L)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+
+    ms_per_block = (t1 - t0) * 1e3 / args.steps
+    attn_ms = [a.elapsed_time(b) for a, b in ev]
+    attn_avg_ms = float(np.mean(attn_ms))
+    flops = attn_flops(cfg)
+    achieved = flops / (attn_avg_ms * 1e-3) / 1e12
+    value = steps * L * flops / (ms_per_block * 1e-3) / 1e12
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_block, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "PR-Sink streamed block at 480x480: H=40, d=128, Q=2700, K=14400 "
+                        f"(Ref 900 + Static/Dynamic/2 window/current 2700 each), {L} layers x "
+                        f"{steps} denoise-step attention calls + {L} clean-KV writes + "
+                        "retrieval/Dynamic copy + bank update",
+            "blocks_timed": f"{args.warmup}..{n_blocks - 1}",
+            "layers": L,
+        },
+        "attn_ms_per_call": round(attn_avg_ms, 5),
+        "attn_ms_p10_p50_p90": [round(float(np.percentile(attn_ms, p)), 5) for p in (10, 50, 90)],
+        "attn_tflops": round(achieved, 2),
+        "attn_frac_bf16_peak": round(achieved / PEAK_BF16_TFLOPS, 4),
+        "ms_per_block": round(ms_per_block, 3),
+        "fps_equiv_12_frames_per_block": round(12.0 / (ms_per_block * 1e-3), 2),
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(achieved, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+            "traffic": None,
+        },
+    }
+
+    if not args.no_cpu_baseline:
+        import oracle as O
+        b = n_blocks
+        orc = O.PRSinkOracle(cfg)
+        fps_h = fps.cpu().numpy()
+        for blk in range(n_blocks):
+            orc.open_block(blk, fps_h[blk])
+            orc.close_block(blk)
+        orc.open_block(b, synth.pose_stream(b + 1, seed=seed)[b])
+        host = lambda t: t.float().cpu().numpy()
+        l = 0
+        q, k, v = (host(x) for x in qkv_pool[0])
+        ref_host = tuple(host(x) for x in synth.ref_kv_torch(cfg, l, seed, dev))
+        block_host = lambda bid: tuple(host(x) for x in clean_pool[(bid * L + l) % POOL])
+        result["cpu_baseline"] = cpu_baseline(cfg, q, k, v, ref_host, block_host, orc,
+                                              args.cpu_budget)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

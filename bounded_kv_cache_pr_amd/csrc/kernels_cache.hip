@@ -1,0 +1,261 @@
+// Cache-maintenance kernels of the PR-Sink path on gfx950:
+//   kv_write     raw K/V [T][H][d] -> slot layout (K [H][t_pad][d], V^T [H][d][t_pad])
+//   slot_copy    whole block slot (all layers) -> another slot; source and
+//                destination come from device state, so no host round trip
+//   retrieve     fingerprint l2-normalisation + argmax over the bank (fp64)
+//   bank_update  exhaustive diversity replacement (fp64)
+#include "prsink_internal.h"
+
+namespace prsink {
+namespace {
+
+// ---------------------------------------------------------------------------
+// kv_write: one workgroup per (64-token tile, head).  K rows are copied
+// straight; V goes through LDS and is written transposed so that attention
+// can feed it to the MFMA B-side without a per-call transpose.
+// ---------------------------------------------------------------------------
+template <typename E>
+__global__ __launch_bounds__(256) void kv_write_kernel(
+    const E* __restrict__ k_src, const E* __restrict__ v_src, E* __restrict__ k_dst0,
+    E* __restrict__ v_dst0, E* __restrict__ k_dst1, E* __restrict__ v_dst1, int n_tok,
+    int n_heads, int head_dim, int t_pad) {
+  constexpr int TT = kKeyTile;
+  constexpr int EPC = 16 / sizeof(E);  // elements per 16-byte chunk
+  extern __shared__ __align__(16) uint8_t smem_raw[];
+  E* smem = reinterpret_cast<E*>(smem_raw);
+  const int n0 = blockIdx.x * TT;
+  const int h = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int cpr = head_dim / EPC;        // chunks per token row
+  const int lds_row = head_dim + EPC;    // padded LDS row, elements
+
+  // K: straight copy; V rows into LDS (zeros past the last token)
+  for (int id = tid; id < TT * cpr; id += blockDim.x) {
+    const int r = id / cpr, c = id % cpr;
+    const int n = n0 + r;
+    uint4 kv = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0);
+    if (n < n_tok) {
+      const size_t src = ((size_t)n * n_heads + h) * head_dim + (size_t)c * EPC;
+      kv = *reinterpret_cast<const uint4*>(k_src + src);
+      vv = *reinterpret_cast<const uint4*>(v_src + src);
+      const size_t dst = ((size_t)h * t_pad + n) * head_dim + (size_t)c * EPC;
+      *reinterpret_cast<uint4*>(k_dst0 + dst) = kv;
+      if (k_dst1) *reinterpret_cast<uint4*>(k_dst1 + dst) = kv;
+    }
+    *reinterpret_cast<uint4*>(smem + r * lds_row + c * EPC) = vv;
+  }
+  __syncthreads();
+  // V^T: row dv of this head holds tokens n0 .. n0+63 (TT/EPC chunks)
+  const int vchunks = TT / EPC;
+  for (int id = tid; id < head_dim * vchunks; id += blockDim.x) {
+    const int dv = id / vchunks, kc = id % vchunks;
+    union { uint4 u; E e[EPC]; } pk;
+#pragma unroll
+    for (int e = 0; e < EPC; ++e) pk.e[e] = smem[(kc * EPC + e) * lds_row + dv];
+    // tokens past n_tok were loaded as zero, so the slot's padding stays zero
+    const size_t dst = ((size_t)h * head_dim + dv) * t_pad + (size_t)(n0 + kc * EPC);
+    *reinterpret_cast<uint4*>(v_dst0 + dst) = pk.u;
+    if (v_dst1) *reinterpret_cast<uint4*>(v_dst1 + dst) = pk.u;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// slot_copy: grid-stride 16-byte copy of one block slot (all layers) to
+// another.  Reads the (source, destination) pair from device state; a
+// negative source means there is nothing to copy.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void slot_copy_kernel(uint8_t* __restrict__ base,
+                                                        size_t slot_bytes,
+                                                        const DevState* __restrict__ st) {
+  const int src = st->copy_src, dst = st->copy_dst;
+  if (src < 0 || src == dst) return;
+  const uint4* __restrict__ s = reinterpret_cast<const uint4*>(base + (size_t)src * slot_bytes);
+  uint4* __restrict__ d = reinterpret_cast<uint4*>(base + (size_t)dst * slot_bytes);
+  const size_t n = slot_bytes / 16;
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  for (; i + 3 * stride < n; i += 4 * stride) {
+    const uint4 a = s[i], b = s[i + stride], c = s[i + 2 * stride], e = s[i + 3 * stride];
+    d[i] = a; d[i + stride] = b; d[i + 2 * stride] = c; d[i + 3 * stride] = e;
+  }
+  for (; i < n; i += stride) d[i] = s[i];
+}
+
+// ---------------------------------------------------------------------------
+// fp64 wave-64 helpers.  Reductions run a fixed butterfly, so results are
+// reproducible bit for bit from run to run.
+// ---------------------------------------------------------------------------
+__device__ inline double wave_sum(double v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+  return v;
+}
+
+__device__ inline double dot_f64(const double* __restrict__ a, const double* __restrict__ b,
+                                 int n, int lane) {
+  double acc = 0.0;
+  for (int k = lane; k < n; k += 64) acc += a[k] * b[k];
+  return wave_sum(acc);
+}
+
+// Fingerprint + retrieval, one wave64.
+__global__ __launch_bounds__(64) void retrieve_kernel(const float* __restrict__ fp_raw,
+                                                      double* __restrict__ phi_cur,
+                                                      const double* __restrict__ bank_phi,
+                                                      DevState* __restrict__ st, int fp_dim,
+                                                      int bank_count, int block, int dyn_slot,
+                                                      int bank_slot0, int32_t* slot_out) {
+  const int lane = threadIdx.x;
+  // phi_b = x / ||x||_2, zero stays zero
+  double ss = 0.0;
+  for (int k = lane; k < fp_dim; k += 64) {
+    const double x = (double)fp_raw[k];
+    ss += x * x;
+  }
+  const double nrm = sqrt(wave_sum(ss));
+  for (int k = lane; k < fp_dim; k += 64) {
+    const double x = (double)fp_raw[k];
+    phi_cur[k] = nrm > 0.0 ? x / nrm : 0.0;
+  }
+  __syncthreads();  // phi_cur is re-read below by other lanes
+  // r(b) = argmax over entries whose id != b-1; strict '>' keeps the lowest slot on ties
+  int r = -1;
+  double best = 0.0;
+  for (int s = 0; s < bank_count; ++s) {
+    const double sc = dot_f64(phi_cur, bank_phi + (size_t)s * fp_dim, fp_dim, lane);
+    if (st->ids[s] == block - 1) continue;
+    if (r < 0 || sc > best) { r = s; best = sc; }
+  }
+  if (lane == 0) {
+    st->last_r = r;
+    if (slot_out) *slot_out = r;
+    if (r >= 0 && st->ids[r] != st->dyn_id) {
+      st->copy_src = bank_slot0 + r;
+      st->copy_dst = dyn_slot;
+      st->dyn_id = st->ids[r];
+    } else {
+      st->copy_src = -1;
+      if (r < 0) st->dyn_id = -1;
+    }
+  }
+}
+
+// Diversity bank update, one wave64.
+__global__ __launch_bounds__(64) void bank_update_kernel(const double* __restrict__ phi_cur,
+                                                         double* __restrict__ bank_phi,
+                                                         DevState* __restrict__ st, int fp_dim,
+                                                         int bank_size, int bank_count, int block,
+                                                         int win_slot, int bank_slot0) {
+  const int lane = threadIdx.x;
+  const int M = bank_size;
+  int dec;  // -1 keep, j = entry to write
+  if (bank_count < M) {
+    dec = bank_count;
+  } else {
+    __shared__ double G[kMaxBank][kMaxBank];  // pairwise dots of the bank, i < j
+    __shared__ double g[kMaxBank];            // dots with the candidate
+    for (int i = 0; i < M; ++i) {
+      const double gi = dot_f64(phi_cur, bank_phi + (size_t)i * fp_dim, fp_dim, lane);
+      if (lane == 0) g[i] = gi;
+      for (int j = i + 1; j < M; ++j) {
+        const double gij = dot_f64(bank_phi + (size_t)i * fp_dim, bank_phi + (size_t)j * fp_dim,
+                                   fp_dim, lane);
+        if (lane == 0) G[i][j] = gij;
+      }
+    }
+    __syncthreads();
+    const double npairs = (double)(M * (M - 1) / 2);
+    // mean pairwise similarity of an option, summed over pairs in slot order
+    double tot = 0.0;
+    for (int i = 0; i < M; ++i)
+      for (int j = i + 1; j < M; ++j) tot += G[i][j];
+    double best = tot / npairs;
+    dec = -1;
+    for (int x = 0; x < M; ++x) {
+      double t = 0.0;
+      for (int i = 0; i < M; ++i)
+        for (int j = i + 1; j < M; ++j) t += (i == x) ? g[j] : (j == x) ? g[i] : G[i][j];
+      const double sx = t / npairs;
+      if (sx < best) { best = sx; dec = x; }
+    }
+  }
+  if (dec >= 0) {
+    for (int k = lane; k < fp_dim; k += 64) bank_phi[(size_t)dec * fp_dim + k] = phi_cur[k];
+  }
+  if (lane == 0) {
+    st->decision = dec;
+    if (dec >= 0) {
+      st->ids[dec] = block;
+      st->copy_src = win_slot;
+      st->copy_dst = bank_slot0 + dec;
+    } else {
+      st->copy_src = -1;
+    }
+  }
+}
+
+__global__ void state_init_kernel(DevState* st) {
+  const int i = threadIdx.x;
+  if (i < kMaxBank) st->ids[i] = -1;
+  if (i == 0) {
+    st->last_r = -1;
+    st->dyn_id = -1;
+    st->decision = -2;
+    st->copy_src = -1;
+    st->copy_dst = -1;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_kv_write(const void* k_src, const void* v_src, void* k_dst0, void* v_dst0,
+                           void* k_dst1, void* v_dst1, int n_tok, int n_heads, int head_dim,
+                           int t_pad, int elem_bytes, hipStream_t s) {
+  dim3 grid((n_tok + kKeyTile - 1) / kKeyTile, n_heads);
+  const size_t lds = (size_t)kKeyTile * (head_dim * elem_bytes + 16);
+  if (elem_bytes == 2) {
+    using E = uint16_t;
+    hipLaunchKernelGGL(kv_write_kernel<E>, grid, dim3(256), lds, s, (const E*)k_src,
+                       (const E*)v_src, (E*)k_dst0, (E*)v_dst0, (E*)k_dst1, (E*)v_dst1, n_tok,
+                       n_heads, head_dim, t_pad);
+  } else {
+    using E = uint32_t;
+    hipLaunchKernelGGL(kv_write_kernel<E>, grid, dim3(256), lds, s, (const E*)k_src,
+                       (const E*)v_src, (E*)k_dst0, (E*)v_dst0, (E*)k_dst1, (E*)v_dst1, n_tok,
+                       n_heads, head_dim, t_pad);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_slot_copy(char* block_base, size_t slot_bytes, const DevState* st,
+                            hipStream_t s) {
+  const size_t n16 = slot_bytes / 16;
+  size_t blocks = (n16 + 255) / 256;
+  if (blocks > 256 * 16) blocks = 256 * 16;
+  hipLaunchKernelGGL(slot_copy_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
+                     reinterpret_cast<uint8_t*>(block_base), slot_bytes, st);
+  return hipGetLastError();
+}
+
+hipError_t launch_retrieve(const float* fp_raw, double* phi_cur, const double* bank_phi,
+                           DevState* st, int fp_dim, int bank_count, int block, int dyn_slot,
+                           int bank_slot0, int32_t* slot_out, hipStream_t s) {
+  hipLaunchKernelGGL(retrieve_kernel, dim3(1), dim3(64), 0, s, fp_raw, phi_cur, bank_phi, st,
+                     fp_dim, bank_count, block, dyn_slot, bank_slot0, slot_out);
+  return hipGetLastError();
+}
+
+hipError_t launch_bank_update(const double* phi_cur, double* bank_phi, DevState* st, int fp_dim,
+                              int bank_size, int bank_count, int block, int win_slot,
+                              int bank_slot0, hipStream_t s) {
+  hipLaunchKernelGGL(bank_update_kernel, dim3(1), dim3(64), 0, s, phi_cur, bank_phi, st, fp_dim,
+                     bank_size, bank_count, block, win_slot, bank_slot0);
+  return hipGetLastError();
+}
+
+hipError_t launch_state_init(DevState* st, hipStream_t s) {
+  hipLaunchKernelGGL(state_init_kernel, dim3(1), dim3(64), 0, s, st);
+  return hipGetLastError();
+}
+
+}  // namespace prsink

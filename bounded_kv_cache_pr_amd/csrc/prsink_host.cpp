@@ -1,0 +1,483 @@
+// Host side of the PR-Sink C ABI: config validation, arena layout, RoPE
+// tables, the per-block state machine, and kernel launches.
+//
+// The cache follows the PR-Sink description: Ref Sink, Static Sink (first
+// generated block), one Dynamic Sink recalled by pose retrieval, and a rolling
+// window of W slots whose last slot is the current block (HF papers abstract
+// of LiveAnimate; papers.ananclaw.com explainer, "Pose-Retrieval Sink
+// Attention" section; paper.rainbus.top review, full-pipeline paragraph).
+// Memory is one caller-owned arena whose size is a closed form of the config,
+// so the footprint cannot grow with the stream (HF abstract: memory and
+// per-block latency independent of stream length).
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "pr_sink.h"
+#include "prsink_internal.h"
+
+using namespace prsink;
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+#define PRS_HIP(x)                                                                     \
+  do {                                                                                 \
+    hipError_t e_ = (x);                                                               \
+    if (e_ != hipSuccess) return fail(PR_SINK_EHIP, "%s: %s", #x, hipGetErrorString(e_)); \
+  } while (0)
+
+constexpr size_t kAlign = 4096;
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+int pad_tokens(int n) { return (n + kKeyTile - 1) / kKeyTile * kKeyTile; }
+
+// Arena layout (offsets in bytes from the arena base):
+//   [state | fingerprints | rope table] [Ref slot] [block slots...]
+// Block slots: Static, Dynamic, window 0..W-1, bank 0..M-1.  Each slot holds,
+// per layer, K [H][t_pad][d] then V^T [H][d][t_pad].
+struct Layout {
+  int elem, tpf, tb, tr, tb_pad, tr_pad;
+  size_t kv_b, layer_b, slot_b;   // block slot: one tensor, one layer, whole slot
+  size_t kv_r, layer_r, slot_r;   // Ref slot
+  size_t off_state, off_phi_bank, off_phi_cur, off_rope, off_ref, off_blocks, total;
+  int n_t, np_t, np_h, np_w, rope_h_off, rope_w_off, rope_entries;
+  int n_block_slots;
+};
+
+bool check_config(const pr_sink_config* c) {
+  if (!c) return fail(PR_SINK_EINVAL, "config is NULL"), false;
+  if (c->n_layers < 1 || c->n_layers > 4096) return fail(PR_SINK_EINVAL, "n_layers out of range"), false;
+  if (c->n_heads < 1 || c->n_heads > 1024) return fail(PR_SINK_EINVAL, "n_heads out of range"), false;
+  if (c->head_dim != 64 && c->head_dim != 128) return fail(PR_SINK_EINVAL, "head_dim must be 64 or 128"), false;
+  int sum = 0;
+  for (int a = 0; a < 3; ++a) {
+    if (c->rope_dims[a] < 2 || c->rope_dims[a] % 2) return fail(PR_SINK_EINVAL, "rope band %d must be even and >= 2", a), false;
+    sum += c->rope_dims[a];
+  }
+  if (sum != c->head_dim) return fail(PR_SINK_EINVAL, "rope bands sum to %d, head_dim is %d", sum, c->head_dim), false;
+  if (!(c->rope_theta > 0.0) || !std::isfinite(c->rope_theta)) return fail(PR_SINK_EINVAL, "rope_theta must be > 0"), false;
+  if (c->lat_h < 1 || c->lat_w < 1 || c->lat_h > 1024 || c->lat_w > 1024) return fail(PR_SINK_EINVAL, "latent size out of range"), false;
+  if (c->ref_frames < 1 || c->block_frames < 1 || c->ref_frames > 64 || c->block_frames > 64) return fail(PR_SINK_EINVAL, "frame counts out of range"), false;
+  if (c->window_slots < 1 || c->window_slots > kMaxSegments - 3) return fail(PR_SINK_EINVAL, "window_slots must be 1..%d", kMaxSegments - 3), false;
+  if (c->bank_size < 2 || c->bank_size > kMaxBank) return fail(PR_SINK_EINVAL, "bank_size must be 2..%d", kMaxBank), false;
+  if (c->bank_fill_blocks < 0) return fail(PR_SINK_EINVAL, "bank_fill_blocks must be >= 0"), false;
+  if (c->fp_dim < 1 || c->fp_dim > 4096) return fail(PR_SINK_EINVAL, "fp_dim must be 1..4096"), false;
+  if (c->dtype != PR_SINK_BF16 && c->dtype != PR_SINK_F32) return fail(PR_SINK_EINVAL, "unknown dtype"), false;
+  if (c->t0 < 0 || c->t0 > (1 << 20)) return fail(PR_SINK_EINVAL, "t0 out of range"), false;
+  const long long tpf = (long long)c->lat_h * c->lat_w;
+  if (tpf * c->block_frames > (1 << 24) || tpf * c->ref_frames > (1 << 24)) return fail(PR_SINK_EINVAL, "block too large"), false;
+  return true;
+}
+
+Layout make_layout(const pr_sink_config* c) {
+  Layout L{};
+  L.elem = c->dtype == PR_SINK_BF16 ? 2 : 4;
+  L.tpf = c->lat_h * c->lat_w;
+  L.tb = L.tpf * c->block_frames;
+  L.tr = L.tpf * c->ref_frames;
+  L.tb_pad = pad_tokens(L.tb);
+  L.tr_pad = pad_tokens(L.tr);
+  const size_t hd = (size_t)c->n_heads * c->head_dim * L.elem;
+  L.kv_b = hd * L.tb_pad;
+  L.layer_b = 2 * L.kv_b;
+  L.slot_b = align_up(L.layer_b * c->n_layers, kAlign);
+  L.kv_r = hd * L.tr_pad;
+  L.layer_r = 2 * L.kv_r;
+  L.slot_r = align_up(L.layer_r * c->n_layers, kAlign);
+  L.n_block_slots = 2 + c->window_slots + c->bank_size;
+  // temporal positions: Ref, Static, Dynamic, W-1 previous blocks, current
+  L.n_t = c->ref_frames + (c->window_slots + 2) * c->block_frames;
+  L.np_t = c->rope_dims[0] / 2;
+  L.np_h = c->rope_dims[1] / 2;
+  L.np_w = c->rope_dims[2] / 2;
+  L.rope_h_off = L.n_t * L.np_t;
+  L.rope_w_off = L.rope_h_off + c->lat_h * L.np_h;
+  L.rope_entries = L.rope_w_off + c->lat_w * L.np_w;
+  size_t off = 0;
+  L.off_state = off;
+  off = align_up(off + sizeof(DevState), 256);
+  L.off_phi_bank = off;
+  off = align_up(off + sizeof(double) * c->bank_size * c->fp_dim, 256);
+  L.off_phi_cur = off;
+  off = align_up(off + sizeof(double) * c->fp_dim, 256);
+  L.off_rope = off;
+  off = align_up(off + sizeof(float) * 2 * L.rope_entries, kAlign);
+  L.off_ref = off;
+  off += L.slot_r;
+  L.off_blocks = off;
+  off += L.slot_b * L.n_block_slots;
+  L.total = off;
+  return L;
+}
+
+// cos/sin of every (band, position, pair), computed in double, stored as float.
+std::vector<float> rope_table(const pr_sink_config* c, const Layout& L) {
+  std::vector<float> t(2 * (size_t)L.rope_entries);
+  auto fill = [&](int base, int npos, int pos0, int band_dim) {
+    const int np = band_dim / 2;
+    for (int ps = 0; ps < npos; ++ps)
+      for (int i = 0; i < np; ++i) {
+        const double w = std::pow(c->rope_theta, -2.0 * i / band_dim);
+        const double a = (double)(pos0 + ps) * w;
+        t[2 * (size_t)(base + ps * np + i)] = (float)std::cos(a);
+        t[2 * (size_t)(base + ps * np + i) + 1] = (float)std::sin(a);
+      }
+  };
+  fill(0, L.n_t, c->t0, c->rope_dims[0]);
+  fill(L.rope_h_off, c->lat_h, 0, c->rope_dims[1]);
+  fill(L.rope_w_off, c->lat_w, 0, c->rope_dims[2]);
+  return t;
+}
+
+}  // namespace
+
+struct pr_sink_cache {
+  pr_sink_config cfg;
+  Layout lay;
+  bool dry;
+  char* arena;
+  int next_block;     // block to open next
+  bool open;
+  int bank_count;     // entries filled so far (the first M blocks are inserted unconditionally)
+  bool dyn_present;   // the open block attends the Dynamic Sink
+  std::vector<uint8_t> ref_set, written;
+
+  char* block_slot(int bs) const { return arena + lay.off_blocks + (size_t)bs * lay.slot_b; }
+  DevState* state() const { return reinterpret_cast<DevState*>(arena + lay.off_state); }
+  double* phi_bank() const { return reinterpret_cast<double*>(arena + lay.off_phi_bank); }
+  double* phi_cur() const { return reinterpret_cast<double*>(arena + lay.off_phi_cur); }
+  const float2* rope() const { return reinterpret_cast<const float2*>(arena + lay.off_rope); }
+  int bs_static() const { return 0; }
+  int bs_dynamic() const { return 1; }
+  int bs_window(int j) const { return 2 + j; }
+  int bs_bank(int i) const { return 2 + cfg.window_slots + i; }
+};
+
+namespace {
+
+hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+int check_layer(const pr_sink_cache* c, int layer) {
+  if (!c) return fail(PR_SINK_EINVAL, "cache is NULL");
+  if (layer < 0 || layer >= c->cfg.n_layers) return fail(PR_SINK_EINVAL, "layer %d out of range", layer);
+  return PR_SINK_OK;
+}
+
+int check_tensor(const void* p, const char* name) {
+  if (!p) return fail(PR_SINK_EINVAL, "%s is NULL", name);
+  if (!aligned16(p)) return fail(PR_SINK_EINVAL, "%s must be 16-byte aligned", name);
+  return PR_SINK_OK;
+}
+
+// Segment token counts and temporal table rows for the open block.
+void segment_table(const pr_sink_cache* c, int* tokens, int* t_index) {
+  const pr_sink_config& g = c->cfg;
+  const int b = c->next_block;
+  const int fb = g.block_frames;
+  int t = 0, s = 0;
+  tokens[s] = c->lay.tr; t_index[s++] = t; t += g.ref_frames;
+  tokens[s] = b >= 1 ? c->lay.tb : 0; t_index[s++] = t; t += fb;          // Static = block 0
+  tokens[s] = c->dyn_present ? c->lay.tb : 0; t_index[s++] = t; t += fb;  // Dynamic
+  for (int j = 0; j < g.window_slots - 1; ++j) {                           // blocks b-(W-1) .. b-1
+    const int id = b - (g.window_slots - 1) + j;
+    tokens[s] = id >= 0 ? c->lay.tb : 0; t_index[s++] = t; t += fb;
+  }
+  tokens[s] = c->lay.tb; t_index[s++] = t;                                 // current block
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t pr_sink_arena_bytes(const pr_sink_config* cfg) {
+  if (!check_config(cfg)) return 0;
+  return make_layout(cfg).total;
+}
+
+int pr_sink_cache_init(const pr_sink_config* cfg, void* arena_dev, size_t arena_bytes,
+                       void* stream, pr_sink_cache** out) {
+  if (!out) return fail(PR_SINK_EINVAL, "out is NULL");
+  *out = nullptr;
+  if (!check_config(cfg)) return PR_SINK_EINVAL;
+  const Layout L = make_layout(cfg);
+  const bool dry = arena_dev == nullptr && arena_bytes == 0;
+  if (!dry) {
+    if (!arena_dev) return fail(PR_SINK_EINVAL, "arena is NULL");
+    if (reinterpret_cast<uintptr_t>(arena_dev) & 255) return fail(PR_SINK_EINVAL, "arena must be 256-byte aligned");
+    if (arena_bytes < L.total)
+      return fail(PR_SINK_ENOSPACE, "arena has %zu bytes, config needs %zu", arena_bytes, L.total);
+    int dev = 0;
+    PRS_HIP(hipGetDevice(&dev));
+    hipDeviceProp_t prop;
+    PRS_HIP(hipGetDeviceProperties(&prop, dev));
+    if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0)
+      return fail(PR_SINK_EHIP, "device %d is %s; this library is built for gfx950", dev, prop.gcnArchName);
+    hipStream_t s = as_stream(stream);
+    char* a = static_cast<char*>(arena_dev);
+    PRS_HIP(hipMemsetAsync(a, 0, L.total, s));  // zero padding keeps masked keys finite
+    std::vector<float> tab = rope_table(cfg, L);
+    PRS_HIP(hipMemcpyAsync(a + L.off_rope, tab.data(), tab.size() * sizeof(float),
+                           hipMemcpyHostToDevice, s));
+    PRS_HIP(launch_state_init(reinterpret_cast<DevState*>(a + L.off_state), s));
+    PRS_HIP(hipStreamSynchronize(s));
+  }
+  pr_sink_cache* c = new (std::nothrow) pr_sink_cache();
+  if (!c) return fail(PR_SINK_EINVAL, "out of host memory");
+  c->cfg = *cfg;
+  c->lay = L;
+  c->dry = dry;
+  c->arena = static_cast<char*>(arena_dev);
+  c->next_block = 0;
+  c->open = false;
+  c->bank_count = 0;
+  c->dyn_present = false;
+  c->ref_set.assign(cfg->n_layers, 0);
+  c->written.assign(cfg->n_layers, 0);
+  *out = c;
+  g_err.clear();
+  return PR_SINK_OK;
+}
+
+int pr_sink_set_ref(pr_sink_cache* c, int32_t layer, const void* k_raw, const void* v_raw,
+                    void* stream) {
+  if (int e = check_layer(c, layer)) return e;
+  if (int e = check_tensor(k_raw, "k_raw")) return e;
+  if (int e = check_tensor(v_raw, "v_raw")) return e;
+  if (c->open) return fail(PR_SINK_ESTATE, "set_ref while block %d is open", c->next_block);
+  if (!c->dry) {
+    const Layout& L = c->lay;
+    char* base = c->arena + L.off_ref + (size_t)layer * L.layer_r;
+    PRS_HIP(launch_kv_write(k_raw, v_raw, base, base + L.kv_r, nullptr, nullptr, L.tr,
+                            c->cfg.n_heads, c->cfg.head_dim, L.tr_pad, L.elem, as_stream(stream)));
+  }
+  c->ref_set[layer] = 1;
+  return PR_SINK_OK;
+}
+
+int pr_sink_retrieve(pr_sink_cache* c, int32_t block, const float* fp_raw_dev,
+                     int32_t* slot_out_dev, void* stream) {
+  if (!c) return fail(PR_SINK_EINVAL, "cache is NULL");
+  if (!fp_raw_dev || (reinterpret_cast<uintptr_t>(fp_raw_dev) & 3)) return fail(PR_SINK_EINVAL, "fp_raw_dev must be a 4-byte aligned device pointer");
+  if (slot_out_dev && (reinterpret_cast<uintptr_t>(slot_out_dev) & 3)) return fail(PR_SINK_EINVAL, "slot_out_dev must be 4-byte aligned");
+  if (c->open) return fail(PR_SINK_ESTATE, "block %d is still open", c->next_block);
+  if (block != c->next_block) return fail(PR_SINK_ESTATE, "expected block %d, got %d", c->next_block, block);
+  for (int l = 0; l < c->cfg.n_layers; ++l)
+    if (!c->ref_set[l]) return fail(PR_SINK_ESTATE, "Ref Sink of layer %d not set", l);
+  // The host knows whether a candidate exists: the first M blocks are always
+  // inserted, so a bank with one entry holds block 0, and a fuller bank holds
+  // several distinct blocks of which at most one is block-1.
+  const bool candidate = c->bank_count >= 2 || (c->bank_count == 1 && block - 1 != 0);
+  if (!c->dry) {
+    hipStream_t s = as_stream(stream);
+    PRS_HIP(launch_retrieve(fp_raw_dev, c->phi_cur(), c->phi_bank(), c->state(), c->cfg.fp_dim,
+                            c->bank_count, block, c->bs_dynamic(), c->bs_bank(0), slot_out_dev, s));
+    PRS_HIP(launch_slot_copy(c->block_slot(0), c->lay.slot_b, c->state(), s));
+  }
+  c->dyn_present = candidate;
+  c->open = true;
+  std::fill(c->written.begin(), c->written.end(), 0);
+  return PR_SINK_OK;
+}
+
+int pr_sink_attend(pr_sink_cache* c, int32_t layer, const void* q_raw, const void* k_cur_raw,
+                   const void* v_cur_raw, void* out, void* stream) {
+  if (int e = check_layer(c, layer)) return e;
+  if (int e = check_tensor(q_raw, "q_raw")) return e;
+  if (int e = check_tensor(k_cur_raw, "k_cur_raw")) return e;
+  if (int e = check_tensor(v_cur_raw, "v_cur_raw")) return e;
+  if (int e = check_tensor(out, "out")) return e;
+  if (out == q_raw || out == k_cur_raw || out == v_cur_raw) return fail(PR_SINK_EINVAL, "out aliases an input");
+  if (!c->open) return fail(PR_SINK_ESTATE, "attend with no open block");
+  if (c->dry) return PR_SINK_OK;
+  const pr_sink_config& g = c->cfg;
+  const Layout& L = c->lay;
+  int tokens[kMaxSegments], t_index[kMaxSegments];
+  segment_table(c, tokens, t_index);
+  const int n_seg = g.window_slots + 3;
+  AttnParams p{};
+  const int64_t D = g.head_dim;
+  auto cached = [&](Segment& sg, const char* slot_base, size_t layer_bytes, size_t kv_bytes, int t_pad) {
+    const char* kb = slot_base + (size_t)layer * layer_bytes;
+    sg.k = kb;
+    sg.v = kb + kv_bytes;
+    sg.k_tok = D;
+    sg.k_head = (int64_t)t_pad * D;
+    sg.v_head = D * t_pad;
+    sg.v_dim = t_pad;
+    sg.v_tok = 1;
+    sg.v_transposed = 1;
+  };
+  const int b = c->next_block;
+  for (int s = 0; s < n_seg; ++s) {
+    Segment& sg = p.seg[s];
+    sg.count = tokens[s];
+    sg.t_index = t_index[s];
+    if (s == 0) {
+      cached(sg, c->arena + L.off_ref, L.layer_r, L.kv_r, L.tr_pad);
+    } else if (s == n_seg - 1) {  // current block, caller's [T][H][d]
+      sg.k = k_cur_raw;
+      sg.v = v_cur_raw;
+      sg.k_tok = (int64_t)g.n_heads * D;
+      sg.k_head = D;
+      sg.v_tok = (int64_t)g.n_heads * D;
+      sg.v_head = D;
+      sg.v_dim = 1;
+      sg.v_transposed = 0;
+    } else {
+      int bs;
+      if (s == 1) bs = c->bs_static();
+      else if (s == 2) bs = c->bs_dynamic();
+      else {
+        const int id = b - (g.window_slots - 1) + (s - 3);
+        bs = c->bs_window(id >= 0 ? id % g.window_slots : 0);
+      }
+      cached(sg, c->block_slot(bs), L.layer_b, L.kv_b, L.tb_pad);
+    }
+  }
+  p.q = q_raw;
+  p.out = out;
+  p.rope = c->rope();
+  p.n_seg = n_seg;
+  p.n_q = L.tb;
+  p.n_heads = g.n_heads;
+  p.lat_w = g.lat_w;
+  p.hw = L.tpf;
+  p.q_t_index = t_index[n_seg - 1];
+  p.np_t = L.np_t;
+  p.np_h = L.np_h;
+  p.np_w = L.np_w;
+  p.rope_h_off = L.rope_h_off;
+  p.rope_w_off = L.rope_w_off;
+  p.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)g.head_dim));
+  PRS_HIP(launch_attention(p, g.dtype, g.head_dim, as_stream(stream)));
+  return PR_SINK_OK;
+}
+
+int pr_sink_clean_kv_write(pr_sink_cache* c, int32_t layer, const void* k_raw, const void* v_raw,
+                           void* stream) {
+  if (int e = check_layer(c, layer)) return e;
+  if (int e = check_tensor(k_raw, "k_raw")) return e;
+  if (int e = check_tensor(v_raw, "v_raw")) return e;
+  if (!c->open) return fail(PR_SINK_ESTATE, "clean_kv_write with no open block");
+  if (c->written[layer]) return fail(PR_SINK_ESTATE, "layer %d already written for block %d", layer, c->next_block);
+  if (!c->dry) {
+    const Layout& L = c->lay;
+    const int b = c->next_block;
+    char* w = c->block_slot(c->bs_window(b % c->cfg.window_slots)) + (size_t)layer * L.layer_b;
+    char* st = b == 0 ? c->block_slot(c->bs_static()) + (size_t)layer * L.layer_b : nullptr;
+    PRS_HIP(launch_kv_write(k_raw, v_raw, w, w + L.kv_b, st, st ? st + L.kv_b : nullptr, L.tb,
+                            c->cfg.n_heads, c->cfg.head_dim, L.tb_pad, L.elem, as_stream(stream)));
+  }
+  c->written[layer] = 1;
+  return PR_SINK_OK;
+}
+
+int pr_sink_bank_update(pr_sink_cache* c, int32_t block, void* stream) {
+  if (!c) return fail(PR_SINK_EINVAL, "cache is NULL");
+  if (!c->open || block != c->next_block) return fail(PR_SINK_ESTATE, "bank_update(%d) but open block is %d", block, c->open ? c->next_block : -1);
+  for (int l = 0; l < c->cfg.n_layers; ++l)
+    if (!c->written[l]) return fail(PR_SINK_ESTATE, "clean K/V of layer %d not written for block %d", l, block);
+  const pr_sink_config& g = c->cfg;
+  if (block < g.bank_fill_blocks) {
+    if (!c->dry) {
+      hipStream_t s = as_stream(stream);
+      PRS_HIP(launch_bank_update(c->phi_cur(), c->phi_bank(), c->state(), g.fp_dim, g.bank_size,
+                                 c->bank_count, block, c->bs_window(block % g.window_slots),
+                                 c->bs_bank(0), s));
+      PRS_HIP(launch_slot_copy(c->block_slot(0), c->lay.slot_b, c->state(), s));
+    }
+    if (c->bank_count < g.bank_size) ++c->bank_count;
+  }
+  c->open = false;
+  c->next_block = block + 1;
+  return PR_SINK_OK;
+}
+
+int pr_sink_bank_state(pr_sink_cache* c, int32_t* ids_host, double* fp_host, int32_t* misc_host,
+                       void* stream) {
+  if (!c) return fail(PR_SINK_EINVAL, "cache is NULL");
+  if (!ids_host) return fail(PR_SINK_EINVAL, "ids_host is NULL");
+  if (c->dry) return fail(PR_SINK_EINVAL, "dry-run cache has no device state");
+  hipStream_t s = as_stream(stream);
+  DevState st;
+  PRS_HIP(hipMemcpyAsync(&st, c->state(), sizeof st, hipMemcpyDeviceToHost, s));
+  if (fp_host)
+    PRS_HIP(hipMemcpyAsync(fp_host, c->phi_bank(), sizeof(double) * c->cfg.bank_size * c->cfg.fp_dim,
+                           hipMemcpyDeviceToHost, s));
+  PRS_HIP(hipStreamSynchronize(s));
+  for (int i = 0; i < c->cfg.bank_size; ++i) ids_host[i] = st.ids[i];
+  if (misc_host) {
+    misc_host[0] = st.last_r;
+    misc_host[1] = st.dyn_id;
+    misc_host[2] = st.decision;
+  }
+  return PR_SINK_OK;
+}
+
+int pr_sink_slot_view(const pr_sink_cache* c, int32_t slot, int32_t layer, void** k_dev,
+                      void** v_dev, int32_t* t_pad_out) {
+  if (int e = check_layer(c, layer)) return e;
+  if (!k_dev || !v_dev || !t_pad_out) return fail(PR_SINK_EINVAL, "NULL output pointer");
+  if (c->dry) return fail(PR_SINK_EINVAL, "dry-run cache has no arena");
+  const Layout& L = c->lay;
+  const int n_slots = 1 + L.n_block_slots;
+  if (slot < 0 || slot >= n_slots) return fail(PR_SINK_EINVAL, "slot %d out of range", slot);
+  char* k;
+  size_t kv;
+  if (slot == PR_SINK_SLOT_REF) {
+    k = c->arena + L.off_ref + (size_t)layer * L.layer_r;
+    kv = L.kv_r;
+    *t_pad_out = L.tr_pad;
+  } else {
+    k = c->block_slot(slot - 1) + (size_t)layer * L.layer_b;
+    kv = L.kv_b;
+    *t_pad_out = L.tb_pad;
+  }
+  *k_dev = k;
+  *v_dev = k + kv;
+  return PR_SINK_OK;
+}
+
+int pr_sink_segments(const pr_sink_cache* c, int32_t* tokens_out, int32_t* t_start_out,
+                     int32_t* n_out) {
+  if (!c) return fail(PR_SINK_EINVAL, "cache is NULL");
+  if (!tokens_out || !t_start_out || !n_out) return fail(PR_SINK_EINVAL, "NULL output pointer");
+  if (!c->open) return fail(PR_SINK_ESTATE, "no open block");
+  int tokens[kMaxSegments], t_index[kMaxSegments];
+  segment_table(c, tokens, t_index);
+  const int n = c->cfg.window_slots + 3;
+  for (int s = 0; s < n; ++s) {
+    tokens_out[s] = tokens[s];
+    t_start_out[s] = c->cfg.t0 + t_index[s];
+  }
+  *n_out = n;
+  return PR_SINK_OK;
+}
+
+int pr_sink_cache_destroy(pr_sink_cache* c) {
+  delete c;
+  return PR_SINK_OK;
+}
+
+const char* pr_sink_last_error(void) { return g_err.c_str(); }
+
+}  // extern "C"

@@ -135,6 +135,41 @@ def step_qkv(cfg: PRSinkConfig, block: int, step: int, layer: int, seed: int):
             normal_tokens(n, cfg, 0.5, seed, TAG_VCUR, block, step, layer))
 
 
+# Device-side generation of the same families for the full-size workloads
+# (hundreds of MB per block).  Each (family, block, step, layer) key seeds its
+# own torch generator; bf16 conversion is round-to-nearest-even.
+def _seed64(key) -> int:
+    return int(np.random.SeedSequence([int(k) & 0xFFFFFFFF for k in key]).generate_state(1, np.uint64)[0] >> 1)
+
+
+def normal_tokens_torch(n_tokens: int, cfg: PRSinkConfig, scale: float, device, *key):
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(_seed64(key))
+    x = torch.randn((n_tokens, cfg.n_heads, cfg.head_dim), generator=g, device=device,
+                    dtype=torch.float32) * scale
+    return x.to(torch.bfloat16 if cfg.dtype == DTYPE_BF16 else torch.float32)
+
+
+def ref_kv_torch(cfg: PRSinkConfig, layer: int, seed: int, device):
+    n = cfg.ref_tokens
+    return (normal_tokens_torch(n, cfg, 0.5, device, seed, TAG_KREF, layer),
+            normal_tokens_torch(n, cfg, 0.5, device, seed, TAG_VREF, layer))
+
+
+def clean_kv_torch(cfg: PRSinkConfig, block: int, layer: int, seed: int, device):
+    n = cfg.block_tokens
+    return (normal_tokens_torch(n, cfg, 0.5, device, seed, TAG_KCLEAN, block, layer),
+            normal_tokens_torch(n, cfg, 0.5, device, seed, TAG_VCLEAN, block, layer))
+
+
+def step_qkv_torch(cfg: PRSinkConfig, block: int, step: int, layer: int, seed: int, device):
+    n = cfg.block_tokens
+    return (normal_tokens_torch(n, cfg, 1.0, device, seed, TAG_Q, block, step, layer),
+            normal_tokens_torch(n, cfg, 0.5, device, seed, TAG_KCUR, block, step, layer),
+            normal_tokens_torch(n, cfg, 0.5, device, seed, TAG_VCUR, block, step, layer))
+
+
 # ----------------------------------------------------------------------------
 # Pose fingerprints: raw 558-vectors, [3 frames][62 keypoints][x, y, conf].
 # ----------------------------------------------------------------------------

@@ -1,0 +1,190 @@
+/*
+ * pr_sink.h -- C ABI of the PR-Sink bounded KV cache for AMD MI355X (gfx950).
+ *
+ * PR-Sink (Pose-Retrieval Sink attention, from LiveAnimate) lets the queries
+ * of the current latent block attend over a cache of fixed size:
+ *   Ref Sink     K/V of the reference image (always attended),
+ *   Static Sink  K/V of the first generated block (kept for good),
+ *   Dynamic Sink K/V of one earlier block recalled by pose retrieval,
+ *   window       the W-1 blocks before the current one (W = 3 slots in all,
+ *                the current block being the last slot),
+ *   current      K/V of the block being denoised (passed by the caller).
+ * Sources: HF papers abstract of LiveAnimate (Static/Dynamic Sink, three-slot
+ * rolling window, memory and latency independent of stream length);
+ * LiveAnimate review on paper.rainbus.top, full-pipeline paragraph (attention
+ * formula over [K_ref; history; current], retrieval, Clean KV Update, RoPE
+ * follow).
+ *
+ * Keys are stored raw (before RoPE) and re-rotated with 3D RoPE at their
+ * *current* cache position inside every attention call ("RoPE follow"; review,
+ * full-pipeline and novelty paragraphs).  Temporal positions are fixed by
+ * slot: Ref at t0, then Static, Dynamic, the previous window blocks (oldest
+ * first) and the current block, each block_frames frames long; spatial
+ * positions are the latent (row, column).  An empty segment is skipped and the
+ * others keep their positions.
+ *
+ * Memory: the caller allocates ONE device arena of pr_sink_arena_bytes(cfg)
+ * bytes and every input/output tensor.  The library never allocates or frees
+ * device memory; its footprint is fixed by the config and does not grow with
+ * the stream.  Layout inside the arena is private, except as exposed by
+ * pr_sink_slot_view().
+ *
+ * Tensor layout at the boundary: q, k, v, out are contiguous [T][H][d] in the
+ * config's element type (bf16 or f32), T = block_frames*lat_h*lat_w tokens in
+ * (frame, row, column) order; Ref tensors have T = ref_frames*lat_h*lat_w.
+ *
+ * Streams: every call is asynchronous on `stream` (a hipStream_t passed as
+ * void*; NULL = the null stream) except pr_sink_cache_init and
+ * pr_sink_bank_state, which synchronise.  Inputs must stay valid until the
+ * work queued on `stream` has run.  One cache must not be driven from two
+ * threads or two streams at once.
+ *
+ * Call order per block b = 0, 1, 2, ...:
+ *   pr_sink_retrieve(b)  ->  pr_sink_attend(layer) any number of times
+ *   -> pr_sink_clean_kv_write(layer) once for every layer
+ *   -> pr_sink_bank_update(b).
+ * pr_sink_set_ref(layer) must have been called for every layer before block 0.
+ * A call out of order returns PR_SINK_ESTATE.
+ *
+ * Errors: every int-returning call returns a pr_sink_status.  Arguments and
+ * call order are validated before anything is queued, so an error leaves the
+ * cache unchanged.  A HIP failure at launch returns PR_SINK_EHIP; the message
+ * of the last failure on the calling thread is pr_sink_last_error().
+ */
+#ifndef PR_SINK_H_
+#define PR_SINK_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PR_SINK_OK = 0,
+  PR_SINK_EINVAL = -1,   /* bad argument or config                          */
+  PR_SINK_ESTATE = -2,   /* call out of order (block protocol)               */
+  PR_SINK_ENOSPACE = -3, /* arena smaller than pr_sink_arena_bytes(cfg)      */
+  PR_SINK_EHIP = -4      /* HIP runtime error, or the device is not gfx950   */
+} pr_sink_status;
+
+typedef enum { PR_SINK_BF16 = 0, PR_SINK_F32 = 1 } pr_sink_dtype;
+
+/* Shape of one cache.  All fields are validated by every call that takes it. */
+typedef struct pr_sink_config {
+  int32_t n_layers;         /* >= 1; each layer has its own K/V in every slot       */
+  int32_t n_heads;          /* >= 1                                                  */
+  int32_t head_dim;         /* 64 or 128                                             */
+  int32_t rope_dims[3];     /* (t, h, w) band widths: even, >= 2, sum == head_dim    */
+  double rope_theta;        /* > 0; pair i of a D-wide band turns by pos*theta^(-2i/D) */
+  int32_t lat_h, lat_w;     /* latent rows and columns per frame, >= 1              */
+  int32_t ref_frames;       /* frames in the Ref Sink, >= 1                         */
+  int32_t block_frames;     /* latent frames per block, >= 1                        */
+  int32_t window_slots;     /* rolling-window slots including the current block, 1..5 */
+  int32_t bank_size;        /* memory-bank entries M, 2..8                           */
+  int32_t bank_fill_blocks; /* blocks b < this update the bank; later it is frozen   */
+  int32_t fp_dim;           /* pose fingerprint length, 1..4096                      */
+  int32_t dtype;            /* pr_sink_dtype of K/V/Q/out                            */
+  int32_t t0;               /* temporal position of the first Ref frame, >= 0        */
+} pr_sink_config;
+
+typedef struct pr_sink_cache pr_sink_cache; /* opaque, host-side handle */
+
+/* Slot ids for pr_sink_slot_view. */
+enum {
+  PR_SINK_SLOT_REF = 0,
+  PR_SINK_SLOT_STATIC = 1,
+  PR_SINK_SLOT_DYNAMIC = 2,
+  PR_SINK_SLOT_WINDOW0 = 3 /* window slot j is PR_SINK_SLOT_WINDOW0 + j; bank entry i
+                              follows the window: PR_SINK_SLOT_WINDOW0 + window_slots + i */
+};
+
+/* Bytes of device arena the config needs (0 if the config is invalid).
+ * Closed form in the config only: never depends on the stream length. */
+size_t pr_sink_arena_bytes(const pr_sink_config* cfg);
+
+/* Creates a cache over `arena_dev` (device memory, >= pr_sink_arena_bytes(cfg)
+ * bytes, 256-byte aligned; owned by the caller, must outlive the cache).
+ * Clears the arena and uploads the RoPE cos/sin tables, then synchronises
+ * `stream`.  With arena_dev == NULL and arena_bytes == 0 it creates a
+ * dry-run cache that validates arguments and call order but never touches a
+ * device.  *out receives the handle. */
+int pr_sink_cache_init(const pr_sink_config* cfg, void* arena_dev, size_t arena_bytes,
+                       void* stream, pr_sink_cache** out);
+
+/* Writes the raw Ref Sink K and V of `layer` (device, [ref_T][H][d]) into the
+ * cache (review, full-pipeline paragraph: K_ref, V_ref).  Allowed while no
+ * block is open. */
+int pr_sink_set_ref(pr_sink_cache* c, int32_t layer, const void* k_raw, const void* v_raw,
+                    void* stream);
+
+/* Opens block `block` (must be the next block).  Normalises the raw pose
+ * fingerprint fp_raw_dev (device float[fp_dim]) to unit l2 norm in fp64 (an
+ * all-zero fingerprint stays zero), scores it by dot product against every
+ * bank entry whose block id is not block-1, takes the argmax (lowest slot on
+ * ties) and copies that entry's K/V of all layers into the Dynamic Sink
+ * (review, full-pipeline paragraph: r(b) = argmax phi_b . phi_i excluding b-1;
+ * novelty paragraph: cosine similarity of l2-normalised fingerprints).  If no
+ * entry is eligible the Dynamic Sink is not attended during this block.
+ * slot_out_dev (device int32, nullable) receives the bank slot or -1. */
+int pr_sink_retrieve(pr_sink_cache* c, int32_t block, const float* fp_raw_dev,
+                     int32_t* slot_out_dev, void* stream);
+
+/* One attention call of the open block for `layer`: rotates q (device,
+ * [T][H][d], raw) at the current block's positions and every cached raw key at
+ * its segment's current position, and writes
+ *   out = softmax(q_rot K_rot^T / sqrt(d)) V
+ * over [Ref; Static; Dynamic; window; current] (review, full-pipeline
+ * paragraph, attention formula; the current block attends to itself without
+ * a mask).  k_cur_raw / v_cur_raw are the current block's raw K/V (device,
+ * [T][H][d]); they are read, not stored.  out may not alias the inputs. */
+int pr_sink_attend(pr_sink_cache* c, int32_t layer, const void* q_raw, const void* k_cur_raw,
+                   const void* v_cur_raw, void* out, void* stream);
+
+/* Clean KV Update, write half: stores the clean raw K/V of the open block for
+ * `layer` (device, [T][H][d]) into its rolling-window slot, and for block 0
+ * also into the Static Sink (review, full-pipeline paragraph; HF abstract:
+ * Static Sink = first generated block).  Once per layer per block. */
+int pr_sink_clean_kv_write(pr_sink_cache* c, int32_t layer, const void* k_raw,
+                           const void* v_raw, void* stream);
+
+/* Closes block `block` (the open one; every layer must have been written).
+ * While block < bank_fill_blocks, updates the memory bank: an empty entry is
+ * filled with (block, phi_b, clean K/V); a full bank takes the option among
+ * [keep, replace entry 0, ..., replace entry M-1] with the smallest mean
+ * pairwise fingerprint similarity, keep winning ties (review, novelty
+ * paragraph: exhaustive replacement minimising mean in-bank similarity;
+ * weaknesses and reproducibility paragraphs: M = 5, frozen after 20 blocks). */
+int pr_sink_bank_update(pr_sink_cache* c, int32_t block, void* stream);
+
+/* Synchronises `stream` and copies the bank to host memory: ids_host
+ * (int32[bank_size], -1 = empty), fp_host (double[bank_size*fp_dim], nullable),
+ * misc_host (int32[3], nullable): {last retrieved slot or -1, block id held in
+ * the Dynamic Sink or -1, last bank decision: -2 none, -1 keep, j >= 0 entry
+ * written}. */
+int pr_sink_bank_state(pr_sink_cache* c, int32_t* ids_host, double* fp_host,
+                       int32_t* misc_host, void* stream);
+
+/* Device pointers to the raw K and V of one slot and layer, for inspection.
+ * K is [H][t_pad][d]; V is stored transposed, [H][d][t_pad]; t_pad (tokens
+ * per head, a multiple of 64; padding is zero) goes to *t_pad_out. */
+int pr_sink_slot_view(const pr_sink_cache* c, int32_t slot, int32_t layer, void** k_dev,
+                      void** v_dev, int32_t* t_pad_out);
+
+/* Segments of the open block in cache order (Ref, Static, Dynamic, W-1
+ * window blocks oldest first, current): token counts (0 = not attended) and
+ * temporal start of each, n_out receives the count (window_slots + 3). */
+int pr_sink_segments(const pr_sink_cache* c, int32_t* tokens_out, int32_t* t_start_out,
+                     int32_t* n_out);
+
+/* Frees the host-side handle (never the arena). */
+int pr_sink_cache_destroy(pr_sink_cache* c);
+
+/* Message of the last error on the calling thread ("" if none). */
+const char* pr_sink_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* PR_SINK_H_ */

@@ -246,9 +246,13 @@ class PRSinkOracle:
         return r
 
     # -- attention ------------------------------------------------------------
-    def assemble(self, k_cur, v_cur, ref_kv, block_kv):
-        """Raw keys, values and their (t, h, w) positions in cache order."""
+    def assemble(self, k_cur, v_cur, ref_kv, block_kv, heads=None):
+        """Raw keys, values and their (t, h, w) positions in cache order.
+
+        ``heads`` optionally keeps a subset of heads (sampled checks at full size).
+        """
         c = self.cfg
+        sel = (lambda x: np.asarray(x)[:, heads]) if heads is not None else np.asarray
         ks, vs, ps = [], [], []
         for kind, bid, t0, nf, present in self.segment_layout():
             if not present:
@@ -259,8 +263,8 @@ class PRSinkOracle:
                 k, v = k_cur, v_cur
             else:
                 k, v = block_kv(bid)
-            ks.append(np.asarray(k, np.float64))
-            vs.append(np.asarray(v, np.float64))
+            ks.append(np.asarray(sel(k), np.float64))
+            vs.append(np.asarray(sel(v), np.float64))
             ps.append(frame_positions(nf, t0, c.lat_h, c.lat_w))
         return np.concatenate(ks), np.concatenate(vs), np.concatenate(ps)
 
@@ -278,13 +282,13 @@ class PRSinkOracle:
         q_rows / heads: optional subsets (sampled checks at full size)
         """
         c = self.cfg
-        k, v, kpos = self.assemble(k_cur, v_cur, ref_kv, block_kv)
+        k, v, kpos = self.assemble(k_cur, v_cur, ref_kv, block_kv, heads)
         qpos = self.query_positions()
         q = np.asarray(q, np.float64)
         if q_rows is not None:
             q, qpos = q[q_rows], qpos[q_rows]
         if heads is not None:
-            q, k, v = q[:, heads], k[:, heads], v[:, heads]
+            q = q[:, heads]
         qr = rope_rotate(q, qpos, c.rope_dims, c.rope_theta)
         kr = rope_rotate(k, kpos, c.rope_dims, c.rope_theta)
         return attention(qr, kr, v, 1.0 / math.sqrt(c.head_dim))
