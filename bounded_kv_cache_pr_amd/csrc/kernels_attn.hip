@@ -2,28 +2,22 @@
 //
 // The current block's queries attend over [Ref; Static; Dynamic; window;
 // current] with scale 1/sqrt(d) (LiveAnimate review on paper.rainbus.top,
-// full-pipeline paragraph, attention formula).  Every key is read raw and
-// rotated with 3D RoPE at its segment's *current* temporal slot and its
-// latent (row, column) before use (same paragraph: raw keys re-rotated at the
-// current cache position; novelty paragraph: reuse decoupled from the
-// original timestamp).
+// full-pipeline paragraph, attention formula and the prose around it: the
+// current block is attended too).  Every key is read raw and rotated with 3D
+// RoPE at its segment's *current* temporal slot and its latent (row, column)
+// before use (same paragraph: raw keys re-rotated at the current cache
+// position; novelty paragraph: reuse decoupled from the original timestamp).
 //
-// bf16 kernel (one workgroup = 4 wave64 = 128 query rows of one head):
-//   * Q rows are rotated once in the prologue and kept in VGPRs as the MFMA
-//     B operand.
-//   * Per 64-key tile, the workgroup stages the keys into LDS rotated (each
-//     key is rotated once per workgroup, in fp32, rounded to bf16) and V^T
-//     (cached V is already stored transposed; the current block's V is
-//     transposed while staging).
-//   * S^T = K_rot Q_rot^T on v_mfma_f32_32x32x16_bf16: a lane owns one query
+// Common structure of the bf16 kernels:
+//   * S^T = K_rot Q_rot^T on v_mfma_f32_32x32x16_bf16.  A lane owns one query
 //     column and 16 key rows of each 32x32 block, so the softmax row max/sum
-//     stay in-lane except for one exchange with lane ^ 32.  Keys are placed
-//     in LDS with bits 2 and 3 of the row index swapped, which makes the
-//     probabilities a lane holds after the QK^T MFMA exactly the B operand of
-//     the PV MFMA, with no shuffles.
-//   * O^T = V^T P^T accumulates in fp32; online softmax in base 2 with the
-//     1/sqrt(d) scale folded in.
-// fp32 kernel: a plain one-query-per-lane loop for the fp32 configuration.
+//     stay in-lane except for one exchange with lane ^ 32.  Keys sit in LDS
+//     with bits 2 and 3 of their row index swapped, which makes the
+//     probabilities a lane holds after QK^T exactly the B operand of the PV
+//     MFMA, with no shuffles.
+//   * O^T = V^T P^T accumulates in fp32; the online softmax runs in base 2
+//     with the 1/sqrt(d) scale folded into one FMA per score.
+// The fp32 kernel is a plain one-query-per-lane loop for fp32 caches.
 #include "prsink_internal.h"
 
 namespace prsink {
@@ -31,7 +25,10 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+__device__ constexpr bf16x2 kOnes = {(__bf16)1.0f, (__bf16)1.0f};
 
 __device__ inline uint32_t pack_bf16(float lo, float hi) {
   bf16x2 v = {(__bf16)lo, (__bf16)hi};  // v_cvt_pk_bf16_f32, round to nearest even
@@ -43,6 +40,11 @@ __device__ inline uint32_t rotate_pair_bf16(uint32_t w, float2 cs) {
   const float x0 = __uint_as_float(w << 16);
   const float x1 = __uint_as_float(w & 0xffff0000u);
   return pack_bf16(x0 * cs.x - x1 * cs.y, x0 * cs.y + x1 * cs.x);
+}
+
+// n / d for the token ranges the host checked: multiply-high, or n itself when d == 1.
+__device__ inline uint32_t div_magic(uint32_t n, uint32_t magic, uint32_t one) {
+  return __umulhi(n, magic) + n * one;
 }
 
 // Where the cos/sin of RoPE pair `pair` live: band base offset, row stride
@@ -68,72 +70,77 @@ __device__ inline float2 pair_cs(const AttnParams& p, const PairTab& t, int tt, 
   return p.rope[t.base + pos * t.stride];
 }
 
+__device__ inline void token_pos(const AttnParams& p, int n, int t_index, int& tt, int& y, int& x) {
+  const int f = div_magic(n, p.magic_hw, p.one_hw), j = n - f * p.hw;
+  y = div_magic(j, p.magic_w, p.one_w);
+  x = j - y * p.lat_w;
+  tt = t_index + f;
+}
+
 // Row r of a 64-row key tile lives at LDS row key_perm(r): bits 2 and 3 swapped.
 __device__ inline int key_perm(int r) { return (r & ~0xC) | ((r & 4) << 1) | ((r & 8) >> 1); }
 
+// Rotates 8 raw bf16 (4 pairs, starting at pair `pair0`) of one row at (tt, y, x).
+__device__ inline bf16x8 rotate_chunk_generic(const AttnParams& p, uint4 w, int pair0, int tt,
+                                              int y, int x) {
+  uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+  for (int e = 0; e < 4; ++e) ws[e] = rotate_pair_bf16(ws[e], pair_cs(p, pair_tab(p, pair0 + e), tt, y, x));
+  return __builtin_bit_cast(bf16x8, make_uint4(ws[0], ws[1], ws[2], ws[3]));
+}
+
+// XCD-aware tile order: consecutive workgroup ids land on different XCDs, so
+// every XCD gets whole heads; the query tiles of a head then share that XCD's
+// L2 while they stream the same keys.
+__device__ inline bool map_workgroup(const AttnParams& p, int& head, int& qt) {
+  const int wg = blockIdx.x;
+  const int xcd = wg & 7, jx = wg >> 3;
+  head = xcd + 8 * (jx / p.n_qtiles);
+  qt = jx % p.n_qtiles;
+  return head < p.n_heads;
+}
+
+// ---------------------------------------------------------------------------
+// Generic bf16 kernel (any RoPE band split): 4 waves x 32 query rows, one
+// 64-key tile staged per iteration through registers.
+// ---------------------------------------------------------------------------
 template <int D>
-__global__ __launch_bounds__(256) void attn_bf16_kernel(const AttnParams p) {
-  constexpr int KT = kKeyTile;      // keys per tile
-  constexpr int QW = 32;            // query rows per wave
-  constexpr int QT = 4 * QW;        // query rows per workgroup
+__global__ __launch_bounds__(256) void attn_bf16_generic(const AttnParams p) {
+  constexpr int KT = kKeyTile;
+  constexpr int QT = 128;
   constexpr int KS = D + 8;         // LDS K row stride (bf16 elements)
   constexpr int VS = KT + 8;        // LDS V^T row stride
-  constexpr int NC = D / 16;        // 16-wide d chunks (QK^T k-steps)
-  constexpr int NDB = D / 32;       // 32-wide dv blocks of O^T
+  constexpr int NC = D / 16;
+  constexpr int NDB = D / 32;
   __shared__ __align__(16) uint16_t Ks[KT * KS];
   __shared__ __align__(16) uint16_t Vs[D * VS];
 
-  // XCD-aware tile order: consecutive workgroup ids land on different XCDs,
-  // so give every XCD whole heads; the query tiles of a head then share that
-  // XCD's L2 while they stream the same keys.
-  const int wg = blockIdx.x;
-  const int xcd = wg & 7, jx = wg >> 3;
-  const int head = xcd + 8 * (jx / p.n_qtiles);
-  const int qt = jx % p.n_qtiles;
-  if (head >= p.n_heads) return;
-
+  int head, qt;
+  if (!map_workgroup(p, head, qt)) return;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int hh = lane >> 5, l32 = lane & 31;
   const int H = p.n_heads;
 
-  // ---- prologue: rotate this lane's query row, keep it as the MFMA B operand
-  const int qrow = qt * QT + wave * QW + l32;
+  const int qrow = qt * QT + wave * 32 + l32;
   const bool qvalid = qrow < p.n_q;
   bf16x8 qreg[NC];
   {
     int tq = 0, yq = 0, xq = 0;
-    if (qvalid) {
-      const int f = qrow / p.hw, rem = qrow - f * p.hw;
-      yq = rem / p.lat_w;
-      xq = rem - yq * p.lat_w;
-      tq = p.q_t_index + f;
-    }
+    if (qvalid) token_pos(p, qrow, p.q_t_index, tq, yq, xq);
     const uint16_t* qp = static_cast<const uint16_t*>(p.q) + ((size_t)qrow * H + head) * D;
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
       const int off = 16 * c + 8 * hh;
-      uint4 w = make_uint4(0, 0, 0, 0);
-      if (qvalid) w = *reinterpret_cast<const uint4*>(qp + off);
-      uint32_t ws[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const PairTab t = pair_tab(p, off / 2 + e);
-        ws[e] = rotate_pair_bf16(ws[e], pair_cs(p, t, tq, yq, xq));
-      }
-      const uint4 r = make_uint4(ws[0], ws[1], ws[2], ws[3]);
-      qreg[c] = __builtin_bit_cast(bf16x8, r);
+      const uint4 w = qvalid ? *reinterpret_cast<const uint4*>(qp + off) : make_uint4(0, 0, 0, 0);
+      qreg[c] = rotate_chunk_generic(p, w, off / 2, tq, yq, xq);
     }
   }
 
-  // ---- staging assignments (fixed per thread)
   constexpr int KCPR = D / 8;             // 16-byte chunks per key row
-  constexpr int KROWS = 256 / KCPR;       // key rows per staging pass
+  constexpr int KROWS = 256 / KCPR;
   const int kcc = tid % KCPR;
   const int kr0 = tid / KCPR;
-  PairTab ktab[4];
-#pragma unroll
-  for (int e = 0; e < 4; ++e) ktab[e] = pair_tab(p, kcc * 4 + e);
 
   f32x16 o[NDB];
 #pragma unroll
@@ -144,48 +151,30 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(const AttnParams p) {
   for (int s = 0; s < p.n_seg; ++s) {
     const Segment sg = p.seg[s];
     const int count = sg.count;
-    const uint16_t* kbase = static_cast<const uint16_t*>(sg.k) + (size_t)head * sg.k_head;
-    const uint16_t* vbase = static_cast<const uint16_t*>(sg.v) + (size_t)head * sg.v_head;
+    const uint16_t* kbase = static_cast<const uint16_t*>(sg.k) + (size_t)head * sg.head;
+    const uint16_t* vbase = static_cast<const uint16_t*>(sg.v) + (size_t)head * sg.head;
     for (int n0 = 0; n0 < count; n0 += KT) {
-      // -- stage K (rotated at this segment's current positions)
 #pragma unroll
       for (int it = 0; it < KT / KROWS; ++it) {
         const int r = kr0 + it * KROWS;
         const int n = n0 + r;
         uint4 w = make_uint4(0, 0, 0, 0);
         if (n < count) {
-          w = *reinterpret_cast<const uint4*>(kbase + (size_t)n * sg.k_tok + kcc * 8);
-          const int f = n / p.hw, rem = n - f * p.hw;
-          const int y = rem / p.lat_w, x = rem - y * p.lat_w;
-          const int tt = sg.t_index + f;
-          w.x = rotate_pair_bf16(w.x, pair_cs(p, ktab[0], tt, y, x));
-          w.y = rotate_pair_bf16(w.y, pair_cs(p, ktab[1], tt, y, x));
-          w.z = rotate_pair_bf16(w.z, pair_cs(p, ktab[2], tt, y, x));
-          w.w = rotate_pair_bf16(w.w, pair_cs(p, ktab[3], tt, y, x));
+          int tt, y, x;
+          token_pos(p, n, sg.t_index, tt, y, x);
+          w = __builtin_bit_cast(uint4, rotate_chunk_generic(
+              p, *reinterpret_cast<const uint4*>(kbase + (size_t)n * sg.tok + kcc * 8), kcc * 4, tt, y, x));
         }
         *reinterpret_cast<uint4*>(&Ks[key_perm(r) * KS + kcc * 8]) = w;
       }
-      // -- stage V^T
-      if (sg.v_transposed) {
-        constexpr int VCPR = KT / 8;        // chunks per V^T row
-        constexpr int VROWS = 256 / VCPR;
-        const int vc = tid % VCPR, vr0 = tid / VCPR;
-#pragma unroll
-        for (int it = 0; it < D / VROWS; ++it) {
-          const int dv = vr0 + it * VROWS;
-          // in bounds: the slot is padded to a multiple of KT with zeros
-          const uint4 w =
-              *reinterpret_cast<const uint4*>(vbase + (size_t)dv * sg.v_dim + n0 + vc * 8);
-          *reinterpret_cast<uint4*>(&Vs[dv * VS + vc * 8]) = w;
-        }
-      } else {
+      {  // V rows -> V^T in LDS
         const int key = tid % KT, cg = tid / KT;
         const int n = n0 + key;
 #pragma unroll
         for (int it = 0; it < D / 32; ++it) {
           const int ch = cg + 4 * it;
           uint4 w = make_uint4(0, 0, 0, 0);
-          if (n < count) w = *reinterpret_cast<const uint4*>(vbase + (size_t)n * sg.v_tok + ch * 8);
+          if (n < count) w = *reinterpret_cast<const uint4*>(vbase + (size_t)n * sg.tok + ch * 8);
           const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
@@ -196,7 +185,6 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(const AttnParams p) {
       }
       __syncthreads();
 
-      // -- S^T = K_rot Q_rot^T for 64 keys x this wave's 32 queries
       f32x16 sc[2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
@@ -207,7 +195,7 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(const AttnParams p) {
           sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[c], sc[kb], 0, 0, 0);
         }
       }
-      // -- online softmax (base 2); register r of block kb holds key kb*32 + (r/8)*16 + hh*8 + r%8
+      // register r of block kb holds key kb*32 + (r/8)*16 + hh*8 + r%8
       float mt = -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -234,13 +222,11 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(const AttnParams p) {
           rs += p0 + p1;
           pw[e] = pack_bf16(p0, p1);
         }
-        const uint4 u = make_uint4(pw[0], pw[1], pw[2], pw[3]);
-        pb[kc] = __builtin_bit_cast(bf16x8, u);
+        pb[kc] = __builtin_bit_cast(bf16x8, make_uint4(pw[0], pw[1], pw[2], pw[3]));
       }
       l_run = l_run * alpha + rs;
 #pragma unroll
       for (int db = 0; db < NDB; ++db) o[db] *= alpha;
-      // -- O^T += V^T P^T
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -252,7 +238,7 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(const AttnParams p) {
     }
   }
 
-  // ---- epilogue: O = O^T / rowsum; register 4g+e of block db is dv = 32db + 8g + 4hh + e
+  // register 4g+e of block db is dv = 32db + 8g + 4hh + e
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
   const float inv = 1.0f / l_tot;
   if (qvalid) {
@@ -266,6 +252,325 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(const AttnParams p) {
         *reinterpret_cast<uint2*>(op + db * 32 + g * 8 + hh * 4) = w;
       }
   }
+}
+
+// ---------------------------------------------------------------------------
+// Fast bf16 kernel for the Wan-style band split (t = d - 4*floor(d/6), h = w =
+// 2*floor(d/6)), the layout of every workload here.
+//   * 4 waves x 64 query rows (two 32-row MFMA column blocks per wave): every
+//     K and V operand read from LDS feeds two MFMAs.
+//   * K and V tiles move global -> LDS by DMA (global_load_lds_dwordx4), no
+//     registers in between.  LDS rows are padded (d=128: 304-byte stride, so
+//     16 consecutive rows start 12 banks apart and the 16-byte operand reads
+//     of a 16-lane phase cover all 64 banks once); every LDS address is then
+//     a per-lane base plus an immediate.  DMA lanes that land in padding are
+//     masked off.  The DMA for tile i+1 is issued before tile i is computed
+//     (double-buffered LDS).
+//   * Each wave rotates, in place, the 16 key rows its own DMA brought in
+//     (RoPE follow), with cos/sin read from an LDS copy of the table.
+//   * V stays row-major; the PV operand (V^T) comes from ds_read_b64_tr_b16,
+//     which returns, within each 16-lane group, lane i element e = the value
+//     lane 4e + i/4 points at, element i%4.
+//   * Ragged tiles (the last of each segment) mask keys past the end in a
+//     short uniform branch; the rest of the step is shared.
+//   * Online softmax rescales lazily: the running max used for exp2 moves
+//     only when a score exceeds it by more than 2^8, so probabilities stay
+//     <= 256 and the O rescale is skipped on most tiles.
+// ---------------------------------------------------------------------------
+template <int D, int DT, int DH>
+struct Bands {
+  static constexpr int NPT = DT / 2, NPH = DH / 2, NPW = (D - DT - DH) / 2;
+  static constexpr int band(int g) { return g < NPT ? 0 : (g < NPT + NPH ? 1 : 2); }
+  static constexpr int start(int b) { return b == 0 ? 0 : (b == 1 ? NPT : NPT + NPH); }
+};
+
+template <int D, int DT, int DH>
+struct FastAttn {
+  using B = Bands<D, DT, DH>;
+  static constexpr int KT = kKeyTile;    // keys per tile
+  static constexpr int QT = 256;         // query rows per workgroup
+  static constexpr int RB = D * 2;       // bytes per key row
+  static constexpr int NS = RB / 16;     // 16-byte slots per row
+  static constexpr int RBP = D == 128 ? RB + 48 : RB + 16;  // padded LDS row stride
+  static constexpr int NU = RBP / 16;    // 16-byte units per padded row
+  static constexpr int TILE = KT * RBP;  // bytes per K or V tile in LDS
+  static constexpr int DMA_PER_WAVE = (16 * NU + 63) / 64;  // 1 KB DMA instructions per wave per tensor
+  static constexpr int NC = D / 16;      // QK^T k-steps
+  static constexpr int NDB = D / 32;     // dv blocks
+  static constexpr int SPL = NS / 4;     // slots each lane rotates (a quarter of a row)
+  static constexpr int PPL = SPL * 4;    // RoPE pairs each lane rotates
+  static constexpr float TAU = 8.0f;     // lazy-rescale threshold, log2 units
+
+  const AttnParams& p;
+  char* kbuf;       // LDS: 2 K tiles
+  char* vbuf;       // LDS: 2 V tiles
+  const char* tab;  // LDS: cos/sin table
+  int head, tid, lane, wave, hh, l32;
+  float sl2, tau_raw;
+  // rotation: this lane's row inside its wave's 16 rows, and the band pattern of its pairs
+  int rot_row, rot_q, b0, b1, esplit, c0, c1;
+
+  bf16x8 qreg[2][NC];
+  f32x16 o[2][NDB];
+  float m_run[2], l_run[2];
+
+  __device__ FastAttn(const AttnParams& p_, char* kb, char* vb, const char* tab_, int head_)
+      : p(p_), kbuf(kb), vbuf(vb), tab(tab_), head(head_) {
+    tid = threadIdx.x;
+    lane = tid & 63;
+    wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    hh = lane >> 5;
+    l32 = lane & 31;
+    sl2 = p.scale_log2;
+    tau_raw = TAU / sl2;
+    rot_row = wave * 16 + (lane >> 2);
+    rot_q = lane & 3;
+    const int g0 = rot_q * PPL;
+    b0 = B::band(g0);
+    b1 = B::band(g0 + PPL - 1);
+    esplit = b0 == b1 ? PPL : B::start(b1) - g0;
+    c0 = (g0 - B::start(b0)) * 8;
+    c1 = (g0 - B::start(b1)) * 8;
+  }
+
+  __device__ void init_queries(int qt) {
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      const int qrow = qt * QT + wave * 64 + qb * 32 + l32;
+      const bool valid = qrow < p.n_q;
+      int tq = 0, yq = 0, xq = 0;
+      if (valid) token_pos(p, qrow, p.q_t_index, tq, yq, xq);
+      const uint16_t* qp = static_cast<const uint16_t*>(p.q) + ((size_t)qrow * p.n_heads + head) * D;
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        const int off = 16 * c + 8 * hh;
+        const uint4 w = valid ? *reinterpret_cast<const uint4*>(qp + off) : make_uint4(0, 0, 0, 0);
+        qreg[qb][c] = rotate_chunk_generic(p, w, off / 2, tq, yq, xq);
+      }
+#pragma unroll
+      for (int i = 0; i < NDB; ++i) o[qb][i] = f32x16{};
+      m_run[qb] = -INFINITY;
+      l_run[qb] = 0.f;
+    }
+  }
+
+  // Queue the DMA of tile (s, n0) into LDS buffer `buf`.  K row r holds key
+  // n0 + key_perm(r), V row r holds key n0 + r; rows past the segment's end
+  // repeat its last key (masked later, and always in bounds).
+  __device__ __forceinline__ void dma_tile(int buf, int s, int n0) {
+    const Segment& sg = p.seg[s];
+    const char* kb = static_cast<const char*>(sg.k) + (size_t)head * sg.head * 2;
+    const char* vb = static_cast<const char*>(sg.v) + (size_t)head * sg.head * 2;
+    const size_t tok_bytes = (size_t)sg.tok * 2;
+    const int last = sg.count - 1;
+    // Wave w fills exactly rows 16w .. 16w+15 (the rows it rotates later), so
+    // its own vmcnt wait covers every byte it reads back.
+    const int wbase = wave * 16 * RBP;
+#pragma unroll
+    for (int i = 0; i < DMA_PER_WAVE; ++i) {
+      const int u = i * 64 + lane;                 // 16-byte unit inside the wave's 16 rows
+      const int rr = u / NU, c = u - rr * NU;
+      if (rr < 16 && c < NS) {                     // padding units are never read
+        const int r = wave * 16 + rr;
+        const int nk = min(n0 + key_perm(r), last);
+        const int nv = min(n0 + r, last);
+        __builtin_amdgcn_global_load_lds(kb + (size_t)nk * tok_bytes + c * 16,
+                                         (__attribute__((address_space(3))) void*)(kbuf + buf * TILE + wbase + i * 1024), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(vb + (size_t)nv * tok_bytes + c * 16,
+                                         (__attribute__((address_space(3))) void*)(vbuf + buf * TILE + wbase + i * 1024), 16, 0, 0);
+      }
+    }
+  }
+
+  // Rotate, in place, the quarter-row of K this lane owns (rows of this wave's own DMA).
+  __device__ __forceinline__ void rotate_tile(int buf, int s, int n0) {
+    const Segment& sg = p.seg[s];
+    const int n = min(n0 + key_perm(rot_row), sg.count - 1);
+    int tt, y, x;
+    token_pos(p, n, sg.t_index, tt, y, x);
+    const int rt = tt * (B::NPT * 8);
+    const int rh = p.rope_h_off * 8 + y * (B::NPH * 8);
+    const int rw = p.rope_w_off * 8 + x * (B::NPW * 8);
+    const int r0 = (b0 == 0 ? rt : (b0 == 1 ? rh : rw)) + c0;
+    const int r1 = (b1 == 0 ? rt : (b1 == 1 ? rh : rw)) + c1;
+    char* base = kbuf + buf * TILE + rot_row * RBP + rot_q * SPL * 16;
+#pragma unroll
+    for (int i = 0; i < SPL; ++i) {
+      const int off = 16 * i;
+      uint4 w = *reinterpret_cast<const uint4*>(base + off);
+      uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int pe = 4 * i + e;
+        const float2 cs = *reinterpret_cast<const float2*>(tab + (pe < esplit ? r0 : r1) + 8 * pe);
+        ws[e] = rotate_pair_bf16(ws[e], cs);
+      }
+      *reinterpret_cast<uint4*>(base + off) = make_uint4(ws[0], ws[1], ws[2], ws[3]);
+    }
+  }
+
+  __device__ __forceinline__ void step(int buf, int n0, int count) {
+    const char* kt = kbuf + buf * TILE;
+    const char* vt = vbuf + buf * TILE;
+    // S^T = K_rot Q_rot^T: [2 key blocks] x [2 query blocks] of 32x32
+    f32x16 sc[2][2];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) { sc[qb][0] = f32x16{}; sc[qb][1] = f32x16{}; }
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const char* kr = kt + l32 * RBP + hh * 16 + c * 32;
+      const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(kr);
+      const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(kr + 32 * RBP);
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        sc[qb][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qreg[qb][c], sc[qb][0], 0, 0, 0);
+        sc[qb][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qreg[qb][c], sc[qb][1], 0, 0, 0);
+      }
+    }
+    // register r of key block kb holds key kb*32 + (r/8)*16 + hh*8 + r%8
+    float mt[2];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      if (n0 + KT > count) {  // ragged tile (uniform): keys past the segment end score -inf
+        const int lim = count - n0 - hh * 8;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (kb * 32 + (r >> 3) * 16 + (r & 7) >= lim) sc[qb][kb][r] = -INFINITY;
+      }
+      float m = sc[qb][0][0];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) m = fmaxf(m, sc[qb][kb][r]);
+      mt[qb] = fmaxf(m, __shfl_xor(m, 32, 64));
+    }
+    if (__any((mt[0] > m_run[0] + tau_raw) | (mt[1] > m_run[1] + tau_raw))) {
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        const float m_new = fmaxf(m_run[qb], mt[qb]);
+        const float alpha = __builtin_amdgcn_exp2f((m_run[qb] - m_new) * sl2);
+        m_run[qb] = m_new;
+        l_run[qb] *= alpha;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) o[qb][db] *= alpha;
+      }
+    }
+    bf16x8 pb[2][4];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      const float mb = m_run[qb] * sl2;
+      float rs = l_run[qb];
+#pragma unroll
+      for (int kc = 0; kc < 4; ++kc) {
+        uint32_t pw[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[qb][kc >> 1][(kc & 1) * 8 + 2 * e], sl2, -mb));
+          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[qb][kc >> 1][(kc & 1) * 8 + 2 * e + 1], sl2, -mb));
+          pw[e] = pack_bf16(p0, p1);
+          // the normaliser sums the same bf16-rounded weights the PV product uses
+          rs = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw[e]), kOnes, rs, false);
+        }
+        pb[qb][kc] = __builtin_bit_cast(bf16x8, make_uint4(pw[0], pw[1], pw[2], pw[3]));
+      }
+      l_run[qb] = rs;
+    }
+    // O^T += V^T P^T.  Lane (dv = 32db + l32, hh) needs keys 16kc + 8hh + j, j = 0..7:
+    // two transpose reads; in each, lane 4e + q of a 16-lane group points at
+    // row 16kc + 8hh + 4rd + e, dims 32db + 16*(group&1) + 4q .. +3.
+    const int grp = lane >> 4, i16 = lane & 15;
+    const char* vl = vt + (8 * hh + (i16 >> 2)) * RBP + (16 * (grp & 1) + 4 * (i16 & 3)) * 2;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int kc = 0; kc < 4; ++kc) {
+        i16x4 h[2];
+#pragma unroll
+        for (int rd = 0; rd < 2; ++rd)
+          h[rd] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) i16x4*)(vl + (16 * kc + 4 * rd) * RBP + 64 * db));
+        const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(h[0], h[1], 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+          o[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[qb][kc], o[qb][db], 0, 0, 0);
+      }
+  }
+
+  __device__ void epilogue(int qt) {
+    // register 4g+e of dv block db is dv = 32db + 8g + 4hh + e
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      const int qrow = qt * QT + wave * 64 + qb * 32 + l32;
+      const float l_tot = l_run[qb] + __shfl_xor(l_run[qb], 32, 64);
+      const float inv = 1.0f / l_tot;
+      if (qrow < p.n_q) {
+        uint16_t* op = static_cast<uint16_t*>(p.out) + ((size_t)qrow * p.n_heads + head) * D;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const uint2 w = make_uint2(pack_bf16(o[qb][db][4 * g] * inv, o[qb][db][4 * g + 1] * inv),
+                                       pack_bf16(o[qb][db][4 * g + 2] * inv, o[qb][db][4 * g + 3] * inv));
+            *reinterpret_cast<uint2*>(op + db * 32 + g * 8 + hh * 4) = w;
+          }
+      }
+    }
+  }
+};
+
+__device__ __forceinline__ void wait_dma() { __builtin_amdgcn_s_waitcnt(0x3f70); }  // vmcnt(0)
+
+template <int D, int DT, int DH>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void attn_bf16_fast(const AttnParams p) {
+  using F = FastAttn<D, DT, DH>;
+  __shared__ __align__(16) char kbuf[2 * F::TILE];
+  __shared__ __align__(16) char vbuf[2 * F::TILE];
+  extern __shared__ __align__(16) char rope_lds[];
+
+  int head, qt;
+  if (!map_workgroup(p, head, qt)) return;
+
+  // cos/sin table -> LDS (read by the key rotation of every tile)
+  {
+    const int n16 = (p.rope_bytes + 15) >> 4;
+    const uint4* src = reinterpret_cast<const uint4*>(p.rope);
+    for (int i = threadIdx.x; i < n16; i += 256) reinterpret_cast<uint4*>(rope_lds)[i] = src[i];
+  }
+  F a(p, kbuf, vbuf, rope_lds, head);
+  int s = 0, n0 = 0;
+  while (s < p.n_seg && p.seg[s].count == 0) ++s;
+  if (s < p.n_seg) a.dma_tile(0, s, n0);
+  a.init_queries(qt);
+  wait_dma();
+  __syncthreads();  // the table is in LDS
+  if (s < p.n_seg) a.rotate_tile(0, s, n0);
+  __syncthreads();
+
+  int buf = 0;
+  while (s < p.n_seg) {
+    int s1 = s, n1 = n0 + F::KT;
+    if (n1 >= p.seg[s1].count) {
+      ++s1;
+      n1 = 0;
+      while (s1 < p.n_seg && p.seg[s1].count == 0) ++s1;
+    }
+    // past the last tile, the current one is loaded again into the idle buffer (never read)
+    const bool has_next = s1 < p.n_seg;
+    const int sl = has_next ? s1 : s, nl = has_next ? n1 : n0;
+    a.dma_tile(buf ^ 1, sl, nl);
+    const int count = p.seg[s].count;
+    a.step(buf, n0, count);
+    wait_dma();
+    a.rotate_tile(buf ^ 1, sl, nl);
+    __syncthreads();
+    buf ^= 1;
+    s = s1;
+    n0 = n1;
+  }
+  a.epilogue(qt);
 }
 
 // ---------------------------------------------------------------------------
@@ -285,12 +590,7 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(const AttnParams p) {
   float q[D];
   {
     int tq = 0, yq = 0, xq = 0;
-    if (qvalid) {
-      const int f = qrow / p.hw, rem = qrow - f * p.hw;
-      yq = rem / p.lat_w;
-      xq = rem - yq * p.lat_w;
-      tq = p.q_t_index + f;
-    }
+    if (qvalid) token_pos(p, qrow, p.q_t_index, tq, yq, xq);
     const float* qp = static_cast<const float*>(p.q) + ((size_t)qrow * H + head) * D;
 #pragma unroll
     for (int i = 0; i < D / 2; ++i) {
@@ -309,19 +609,19 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(const AttnParams p) {
   for (int s = 0; s < p.n_seg; ++s) {
     const Segment sg = p.seg[s];
     const int count = sg.count;
-    const float* kbase = static_cast<const float*>(sg.k) + (size_t)head * sg.k_head;
-    const float* vbase = static_cast<const float*>(sg.v) + (size_t)head * sg.v_head;
+    const float* kbase = static_cast<const float*>(sg.k) + (size_t)head * sg.head;
+    const float* vbase = static_cast<const float*>(sg.v) + (size_t)head * sg.head;
     for (int n0 = 0; n0 < count; n0 += KT) {
       for (int id = lane; id < KT * (D / 2); id += KT) {
         const int r = id / (D / 2), pr = id % (D / 2);
         const int n = n0 + r;
         float y0 = 0.f, y1 = 0.f;
         if (n < count) {
-          const float x0 = kbase[(size_t)n * sg.k_tok + 2 * pr];
-          const float x1 = kbase[(size_t)n * sg.k_tok + 2 * pr + 1];
-          const int f = n / p.hw, rem = n - f * p.hw;
-          const int y = rem / p.lat_w, x = rem - y * p.lat_w;
-          const float2 cs = pair_cs(p, pair_tab(p, pr), sg.t_index + f, y, x);
+          const float x0 = kbase[(size_t)n * sg.tok + 2 * pr];
+          const float x1 = kbase[(size_t)n * sg.tok + 2 * pr + 1];
+          int tt, y, x;
+          token_pos(p, n, sg.t_index, tt, y, x);
+          const float2 cs = pair_cs(p, pair_tab(p, pr), tt, y, x);
           y0 = x0 * cs.x - x1 * cs.y;
           y1 = x0 * cs.y + x1 * cs.x;
         }
@@ -329,14 +629,9 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(const AttnParams p) {
         Ks[r][2 * pr + 1] = y1;
       }
       for (int id = lane; id < KT * D; id += KT) {
-        int r, dv;
-        if (sg.v_transposed) { r = id % KT; dv = id / KT; }
-        else { r = id / D; dv = id % D; }
+        const int r = id / D, dv = id % D;
         const int n = n0 + r;
-        float v = 0.f;
-        if (n < count)
-          v = sg.v_transposed ? vbase[(size_t)dv * sg.v_dim + n] : vbase[(size_t)n * sg.v_tok + dv];
-        Vs[r][dv] = v;
+        Vs[r][dv] = n < count ? vbase[(size_t)n * sg.tok + dv] : 0.f;
       }
       __syncthreads();
       const int nk = min(KT, count - n0);
@@ -368,15 +663,25 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(const AttnParams p) {
 
 hipError_t launch_attention(const AttnParams& p_in, int dtype, int head_dim, hipStream_t s) {
   AttnParams p = p_in;
+  const int heads_per_xcd = (p.n_heads + 7) / 8;
   if (dtype == 0) {  // bf16
-    const int qt = 128;
-    p.n_qtiles = (p.n_q + qt - 1) / qt;
-    const int heads_per_xcd = (p.n_heads + 7) / 8;
-    const dim3 grid(8 * heads_per_xcd * p.n_qtiles);
-    if (head_dim == 128)
-      hipLaunchKernelGGL(attn_bf16_kernel<128>, grid, dim3(256), 0, s, p);
-    else
-      hipLaunchKernelGGL(attn_bf16_kernel<64>, grid, dim3(256), 0, s, p);
+    const bool wan = p.np_h == p.np_w && p.np_h == head_dim / 6 && p.rope_bytes <= kMaxRopeLdsBytes;
+    if (wan && (head_dim == 128 || head_dim == 64)) {
+      p.n_qtiles = (p.n_q + 255) / 256;
+      const dim3 grid(8 * heads_per_xcd * p.n_qtiles);
+      const size_t lds = ((size_t)p.rope_bytes + 15) / 16 * 16;
+      if (head_dim == 128)
+        hipLaunchKernelGGL((attn_bf16_fast<128, 44, 42>), grid, dim3(256), lds, s, p);
+      else
+        hipLaunchKernelGGL((attn_bf16_fast<64, 24, 20>), grid, dim3(256), lds, s, p);
+    } else {
+      p.n_qtiles = (p.n_q + 127) / 128;
+      const dim3 grid(8 * heads_per_xcd * p.n_qtiles);
+      if (head_dim == 128)
+        hipLaunchKernelGGL(attn_bf16_generic<128>, grid, dim3(256), 0, s, p);
+      else
+        hipLaunchKernelGGL(attn_bf16_generic<64>, grid, dim3(256), 0, s, p);
+    }
   } else {
     p.n_qtiles = (p.n_q + kKeyTile - 1) / kKeyTile;
     const dim3 grid(p.n_qtiles, p.n_heads);

@@ -1,5 +1,5 @@
 // Cache-maintenance kernels of the PR-Sink path on gfx950:
-//   kv_write     raw K/V [T][H][d] -> slot layout (K [H][t_pad][d], V^T [H][d][t_pad])
+//   kv_write     raw K/V [T][H][d] -> slot layout [H][t_pad][d]
 //   slot_copy    whole block slot (all layers) -> another slot; source and
 //                destination come from device state, so no host round trip
 //   retrieve     fingerprint l2-normalisation + argmax over the bank (fp64)
@@ -10,52 +10,26 @@ namespace prsink {
 namespace {
 
 // ---------------------------------------------------------------------------
-// kv_write: one workgroup per (64-token tile, head).  K rows are copied
-// straight; V goes through LDS and is written transposed so that attention
-// can feed it to the MFMA B-side without a per-call transpose.
+// kv_write: raw K and V [T][H][d] -> slot layout [H][t_pad][d], optionally to
+// a second destination.  Each thread moves 16-byte chunks; rows past T (the
+// slot's padding) are never written, so they stay zero.
 // ---------------------------------------------------------------------------
-template <typename E>
 __global__ __launch_bounds__(256) void kv_write_kernel(
-    const E* __restrict__ k_src, const E* __restrict__ v_src, E* __restrict__ k_dst0,
-    E* __restrict__ v_dst0, E* __restrict__ k_dst1, E* __restrict__ v_dst1, int n_tok,
-    int n_heads, int head_dim, int t_pad) {
-  constexpr int TT = kKeyTile;
-  constexpr int EPC = 16 / sizeof(E);  // elements per 16-byte chunk
-  extern __shared__ __align__(16) uint8_t smem_raw[];
-  E* smem = reinterpret_cast<E*>(smem_raw);
-  const int n0 = blockIdx.x * TT;
-  const int h = blockIdx.y;
-  const int tid = threadIdx.x;
-  const int cpr = head_dim / EPC;        // chunks per token row
-  const int lds_row = head_dim + EPC;    // padded LDS row, elements
-
-  // K: straight copy; V rows into LDS (zeros past the last token)
-  for (int id = tid; id < TT * cpr; id += blockDim.x) {
-    const int r = id / cpr, c = id % cpr;
-    const int n = n0 + r;
-    uint4 kv = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0);
-    if (n < n_tok) {
-      const size_t src = ((size_t)n * n_heads + h) * head_dim + (size_t)c * EPC;
-      kv = *reinterpret_cast<const uint4*>(k_src + src);
-      vv = *reinterpret_cast<const uint4*>(v_src + src);
-      const size_t dst = ((size_t)h * t_pad + n) * head_dim + (size_t)c * EPC;
-      *reinterpret_cast<uint4*>(k_dst0 + dst) = kv;
-      if (k_dst1) *reinterpret_cast<uint4*>(k_dst1 + dst) = kv;
-    }
-    *reinterpret_cast<uint4*>(smem + r * lds_row + c * EPC) = vv;
-  }
-  __syncthreads();
-  // V^T: row dv of this head holds tokens n0 .. n0+63 (TT/EPC chunks)
-  const int vchunks = TT / EPC;
-  for (int id = tid; id < head_dim * vchunks; id += blockDim.x) {
-    const int dv = id / vchunks, kc = id % vchunks;
-    union { uint4 u; E e[EPC]; } pk;
-#pragma unroll
-    for (int e = 0; e < EPC; ++e) pk.e[e] = smem[(kc * EPC + e) * lds_row + dv];
-    // tokens past n_tok were loaded as zero, so the slot's padding stays zero
-    const size_t dst = ((size_t)h * head_dim + dv) * t_pad + (size_t)(n0 + kc * EPC);
-    *reinterpret_cast<uint4*>(v_dst0 + dst) = pk.u;
-    if (v_dst1) *reinterpret_cast<uint4*>(v_dst1 + dst) = pk.u;
+    const uint4* __restrict__ k_src, const uint4* __restrict__ v_src, uint4* __restrict__ k_dst0,
+    uint4* __restrict__ v_dst0, uint4* __restrict__ k_dst1, uint4* __restrict__ v_dst1,
+    int n_tok, int n_heads, int row_chunks, int t_pad) {
+  const size_t total = (size_t)n_tok * n_heads * row_chunks;
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += stride) {
+    const size_t row = i / row_chunks;              // (token, head) row of the source
+    const int c = (int)(i - row * row_chunks);
+    const int h = (int)(row % n_heads);
+    const size_t n = row / n_heads;
+    const size_t dst = ((size_t)h * t_pad + n) * row_chunks + c;
+    const uint4 kv = k_src[i], vv = v_src[i];
+    k_dst0[dst] = kv;
+    v_dst0[dst] = vv;
+    if (k_dst1) { k_dst1[dst] = kv; v_dst1[dst] = vv; }
   }
 }
 
@@ -211,19 +185,15 @@ __global__ void state_init_kernel(DevState* st) {
 hipError_t launch_kv_write(const void* k_src, const void* v_src, void* k_dst0, void* v_dst0,
                            void* k_dst1, void* v_dst1, int n_tok, int n_heads, int head_dim,
                            int t_pad, int elem_bytes, hipStream_t s) {
-  dim3 grid((n_tok + kKeyTile - 1) / kKeyTile, n_heads);
-  const size_t lds = (size_t)kKeyTile * (head_dim * elem_bytes + 16);
-  if (elem_bytes == 2) {
-    using E = uint16_t;
-    hipLaunchKernelGGL(kv_write_kernel<E>, grid, dim3(256), lds, s, (const E*)k_src,
-                       (const E*)v_src, (E*)k_dst0, (E*)v_dst0, (E*)k_dst1, (E*)v_dst1, n_tok,
-                       n_heads, head_dim, t_pad);
-  } else {
-    using E = uint32_t;
-    hipLaunchKernelGGL(kv_write_kernel<E>, grid, dim3(256), lds, s, (const E*)k_src,
-                       (const E*)v_src, (E*)k_dst0, (E*)v_dst0, (E*)k_dst1, (E*)v_dst1, n_tok,
-                       n_heads, head_dim, t_pad);
-  }
+  const int row_chunks = head_dim * elem_bytes / 16;
+  const size_t total = (size_t)n_tok * n_heads * row_chunks;
+  size_t blocks = (total + 255) / 256;
+  if (blocks > 256 * 8) blocks = 256 * 8;
+  hipLaunchKernelGGL(kv_write_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
+                     static_cast<const uint4*>(k_src), static_cast<const uint4*>(v_src),
+                     static_cast<uint4*>(k_dst0), static_cast<uint4*>(v_dst0),
+                     static_cast<uint4*>(k_dst1), static_cast<uint4*>(v_dst1), n_tok, n_heads,
+                     row_chunks, t_pad);
   return hipGetLastError();
 }
 

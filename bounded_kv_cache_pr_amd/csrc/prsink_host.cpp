@@ -48,10 +48,24 @@ constexpr size_t kAlign = 4096;
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 int pad_tokens(int n) { return (n + kKeyTile - 1) / kKeyTile * kKeyTile; }
 
+// Multiply-high divisor: n / d == umulhi(n, ceil(2^32 / d)) for every n with
+// n * (ceil(2^32/d) * d - 2^32) < 2^32.  0 encodes d == 1.
+uint32_t magic_for(uint32_t d) {
+  if (d <= 1) return 0;
+  return (uint32_t)(((1ull << 32) + d - 1) / d);
+}
+
+bool magic_exact(uint32_t d, uint32_t n_max) {
+  if (d <= 1) return true;
+  const unsigned long long m = magic_for(d);
+  const unsigned long long e = m * d - (1ull << 32);
+  return (unsigned long long)n_max * e < (1ull << 32);
+}
+
 // Arena layout (offsets in bytes from the arena base):
 //   [state | fingerprints | rope table] [Ref slot] [block slots...]
 // Block slots: Static, Dynamic, window 0..W-1, bank 0..M-1.  Each slot holds,
-// per layer, K [H][t_pad][d] then V^T [H][d][t_pad].
+// per layer, K [H][t_pad][d] then V [H][t_pad][d].
 struct Layout {
   int elem, tpf, tb, tr, tb_pad, tr_pad;
   size_t kv_b, layer_b, slot_b;   // block slot: one tensor, one layer, whole slot
@@ -83,6 +97,9 @@ bool check_config(const pr_sink_config* c) {
   if (c->t0 < 0 || c->t0 > (1 << 20)) return fail(PR_SINK_EINVAL, "t0 out of range"), false;
   const long long tpf = (long long)c->lat_h * c->lat_w;
   if (tpf * c->block_frames > (1 << 24) || tpf * c->ref_frames > (1 << 24)) return fail(PR_SINK_EINVAL, "block too large"), false;
+  const uint32_t n_max = (uint32_t)(tpf * (c->block_frames > c->ref_frames ? c->block_frames : c->ref_frames));
+  if (!magic_exact((uint32_t)tpf, n_max) || !magic_exact((uint32_t)c->lat_w, (uint32_t)tpf))
+    return fail(PR_SINK_EINVAL, "latent frame %dx%d too large for 32-bit position division", c->lat_h, c->lat_w), false;
   return true;
 }
 
@@ -319,12 +336,8 @@ int pr_sink_attend(pr_sink_cache* c, int32_t layer, const void* q_raw, const voi
     const char* kb = slot_base + (size_t)layer * layer_bytes;
     sg.k = kb;
     sg.v = kb + kv_bytes;
-    sg.k_tok = D;
-    sg.k_head = (int64_t)t_pad * D;
-    sg.v_head = D * t_pad;
-    sg.v_dim = t_pad;
-    sg.v_tok = 1;
-    sg.v_transposed = 1;
+    sg.tok = D;
+    sg.head = (int64_t)t_pad * D;
   };
   const int b = c->next_block;
   for (int s = 0; s < n_seg; ++s) {
@@ -336,12 +349,8 @@ int pr_sink_attend(pr_sink_cache* c, int32_t layer, const void* q_raw, const voi
     } else if (s == n_seg - 1) {  // current block, caller's [T][H][d]
       sg.k = k_cur_raw;
       sg.v = v_cur_raw;
-      sg.k_tok = (int64_t)g.n_heads * D;
-      sg.k_head = D;
-      sg.v_tok = (int64_t)g.n_heads * D;
-      sg.v_head = D;
-      sg.v_dim = 1;
-      sg.v_transposed = 0;
+      sg.tok = (int64_t)g.n_heads * D;
+      sg.head = D;
     } else {
       int bs;
       if (s == 1) bs = c->bs_static();
@@ -367,7 +376,12 @@ int pr_sink_attend(pr_sink_cache* c, int32_t layer, const void* q_raw, const voi
   p.np_w = L.np_w;
   p.rope_h_off = L.rope_h_off;
   p.rope_w_off = L.rope_w_off;
+  p.rope_bytes = L.rope_entries * 8;
   p.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)g.head_dim));
+  p.magic_hw = magic_for((uint32_t)L.tpf);
+  p.one_hw = L.tpf == 1;
+  p.magic_w = magic_for((uint32_t)g.lat_w);
+  p.one_w = g.lat_w == 1;
   PRS_HIP(launch_attention(p, g.dtype, g.head_dim, as_stream(stream)));
   return PR_SINK_OK;
 }

@@ -11,20 +11,17 @@ namespace prsink {
 constexpr int kMaxSegments = 8;   // Ref, Static, Dynamic, <= 4 previous window blocks, current
 constexpr int kMaxBank = 8;
 constexpr int kKeyTile = 64;      // keys per attention tile; slot token counts pad to this
+constexpr int kMaxRopeLdsBytes = 48 * 1024;  // cos/sin table size the fast kernel stages in LDS
 
-// One attended segment of the cache as the attention kernel sees it.
+// One attended segment of the cache as the attention kernel sees it.  K and V
+// share one layout: element (token n, head h, dim i) is at n*tok + h*head + i.
 struct Segment {
-  const void* k;        // raw keys of head 0, token 0
-  const void* v;        // values of head 0 (token 0 / dim 0)
-  int64_t k_tok;        // elements between consecutive tokens of one head
-  int64_t k_head;       // elements between heads
-  int64_t v_head;       // elements between heads
-  int64_t v_tok;        // row-major V: elements between tokens (V^T: unused)
-  int64_t v_dim;        // V^T: elements between dims (= t_pad)  (row-major: unused)
+  const void* k;        // raw keys, head 0, token 0
+  const void* v;        // values, head 0, token 0
+  int64_t tok;          // elements between consecutive tokens of one head
+  int64_t head;         // elements between heads
   int32_t count;        // tokens attended (0 = segment empty)
   int32_t t_index;      // temporal table row of the segment's first frame
-  int32_t v_transposed; // 1: V stored [H][d][t_pad]; 0: V row-major like K
-  int32_t pad_;
 };
 
 struct AttnParams {
@@ -40,8 +37,14 @@ struct AttnParams {
   int32_t q_t_index;    // temporal table row of the current block's first frame
   int32_t np_t, np_h, np_w;   // RoPE pairs per band
   int32_t rope_h_off, rope_w_off;  // float2 offsets of the h and w tables
+  int32_t rope_bytes;   // size of the whole cos/sin table
   int32_t n_qtiles;
   float scale_log2;     // log2(e) / sqrt(d)
+  // n / hw == umulhi(n, magic_hw) + n * one_hw and j / lat_w == umulhi(j, magic_w) +
+  // j * one_w over the token ranges used (checked on the host); a divisor of 1 has
+  // magic 0 and one 1.
+  uint32_t magic_hw, one_hw;
+  uint32_t magic_w, one_w;
 };
 
 // Bank / retrieval state kept in device memory inside the arena.

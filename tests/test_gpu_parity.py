@@ -103,14 +103,11 @@ class Stream:
         kt, vt = self.cache.slot_view(slot, layer)
         k, v = self.clean(block, layer)
         T = self.cfg.block_tokens
-        ks = torch.from_numpy(np.ascontiguousarray(k.transpose(1, 0, 2))).to(self.dt)
-        vs = torch.from_numpy(np.ascontiguousarray(v.transpose(1, 2, 0))).to(self.dt)
-        kt, vt = kt.cpu(), vt.cpu()
-        assert torch.equal(kt[:, :T, :].view(torch.int16 if self.dt == torch.bfloat16 else torch.int32),
-                           ks.view(torch.int16 if self.dt == torch.bfloat16 else torch.int32))
-        assert torch.equal(vt[:, :, :T].contiguous().view(torch.int16 if self.dt == torch.bfloat16 else torch.int32),
-                           vs.view(torch.int16 if self.dt == torch.bfloat16 else torch.int32))
-        assert not kt[:, T:, :].any() and not vt[:, :, T:].any()
+        bits = torch.int16 if self.dt == torch.bfloat16 else torch.int32
+        for got, src in ((kt.cpu(), k), (vt.cpu(), v)):
+            want = torch.from_numpy(np.ascontiguousarray(src.transpose(1, 0, 2))).to(self.dt)
+            assert torch.equal(got[:, :T, :].contiguous().view(bits), want.view(bits))
+            assert not got[:, T:, :].any()
 
 
 def test_c0_stream_30_blocks_fp32():
