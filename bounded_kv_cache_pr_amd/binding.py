@@ -209,7 +209,7 @@ class PRSinkCache:
         return [(int(tok[i]), int(ts[i])) for i in range(n.value)]
 
     def slot_view(self, slot: int, layer: int):
-        """Torch views of one slot's raw K and V, both [H][t_pad][d]."""
+        """Torch views of one slot's raw K and V, both [t_pad][H][d]."""
         k, v, tp = c_void_p(), c_void_p(), c_int32()
         check(lib().pr_sink_slot_view(self._h, slot, layer, byref(k), byref(v), byref(tp)))
         c = self.cfg
@@ -218,7 +218,7 @@ class PRSinkCache:
         base = self.arena.data_ptr()
         kt = self.arena[k.value - base:k.value - base + n * esz].view(self.torch_dtype)
         vt = self.arena[v.value - base:v.value - base + n * esz].view(self.torch_dtype)
-        return (kt.view(c.n_heads, tp.value, c.head_dim), vt.view(c.n_heads, tp.value, c.head_dim))
+        return (kt.view(tp.value, c.n_heads, c.head_dim), vt.view(tp.value, c.n_heads, c.head_dim))
 
     def slot_index_bank(self, i: int) -> int:
         return SLOT_WINDOW0 + self.cfg.window_slots + i

@@ -30,6 +30,11 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 __device__ constexpr bf16x2 kOnes = {(__bf16)1.0f, (__bf16)1.0f};
 
+// Fourth dword of a gfx9 raw buffer resource (32-bit data format).
+constexpr int kBufferConfig = 0x00020000;
+// A buffer offset beyond every range the kernels build (ranges stay < 2^31).
+constexpr uint32_t kOutOfRange = 0x80000000u;
+
 __device__ inline uint32_t pack_bf16(float lo, float hi) {
   bf16x2 v = {(__bf16)lo, (__bf16)hi};  // v_cvt_pk_bf16_f32, round to nearest even
   return __builtin_bit_cast(uint32_t, v);
@@ -299,30 +304,31 @@ struct FastAttn {
   static constexpr int NDB = D / 32;     // dv blocks
   static constexpr int SPL = NS / 4;     // slots each lane rotates (a quarter of a row)
   static constexpr int PPL = SPL * 4;    // RoPE pairs each lane rotates
-  static constexpr float TAU = 8.0f;     // lazy-rescale threshold, log2 units
+  // A tile whose partial row sum of probabilities exceeds this takes the slow
+  // path (exact tile max, rescale).  Below it every probability is < 2^14.
+  static constexpr float SUM_LIMIT = 16384.0f;
 
   const AttnParams& p;
-  char* kbuf;       // LDS: 2 K tiles
-  char* vbuf;       // LDS: 2 V tiles
-  const char* tab;  // LDS: cos/sin table
+  const char* tab;  // LDS: packed-bf16 rotation table
   int head, tid, lane, wave, hh, l32;
-  float sl2, tau_raw;
+  float sl2;
   // rotation: this lane's row inside its wave's 16 rows, and the band pattern of its pairs
   int rot_row, rot_q, b0, b1, esplit, c0, c1;
+
+  uint32_t voff_k[DMA_PER_WAVE], voff_v[DMA_PER_WAVE];
 
   bf16x8 qreg[2][NC];
   f32x16 o[2][NDB];
   float m_run[2], l_run[2];
 
-  __device__ FastAttn(const AttnParams& p_, char* kb, char* vb, const char* tab_, int head_)
-      : p(p_), kbuf(kb), vbuf(vb), tab(tab_), head(head_) {
+  __device__ FastAttn(const AttnParams& p_, const char* tab_, int head_)
+      : p(p_), tab(tab_), head(head_) {
     tid = threadIdx.x;
     lane = tid & 63;
     wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     hh = lane >> 5;
     l32 = lane & 31;
     sl2 = p.scale_log2;
-    tau_raw = TAU / sl2;
     rot_row = wave * 16 + (lane >> 2);
     rot_q = lane & 3;
     const int g0 = rot_q * PPL;
@@ -331,6 +337,17 @@ struct FastAttn {
     esplit = b0 == b1 ? PPL : B::start(b1) - g0;
     c0 = (g0 - B::start(b0)) * 8;
     c1 = (g0 - B::start(b1)) * 8;
+    // DMA unit i*64 + lane of this wave's 16 padded rows -> (row, 16-byte slot)
+    const uint32_t tok_bytes = (uint32_t)(p.n_heads * D * 2);
+#pragma unroll
+    for (int i = 0; i < DMA_PER_WAVE; ++i) {
+      const int u = i * 64 + lane;
+      const int rr = u / NU, c = u - rr * NU;
+      const int r = wave * 16 + rr;
+      const bool data = rr < 16 && c < NS;
+      voff_k[i] = data ? (uint32_t)key_perm(r) * tok_bytes + c * 16 : kOutOfRange;
+      voff_v[i] = data ? (uint32_t)r * tok_bytes + c * 16 : kOutOfRange;
+    }
   }
 
   __device__ void init_queries(int qt) {
@@ -354,36 +371,42 @@ struct FastAttn {
     }
   }
 
-  // Queue the DMA of tile (s, n0) into LDS buffer `buf`.  K row r holds key
-  // n0 + key_perm(r), V row r holds key n0 + r; rows past the segment's end
-  // repeat its last key (masked later, and always in bounds).
-  __device__ __forceinline__ void dma_tile(int buf, int s, int n0) {
+  // Queue the DMA of tile (s, n0) into LDS tiles kdst / vdst.  K row r holds
+  // key n0 + key_perm(r), V row r holds key n0 + r; rows past the segment's
+  // end repeat its last key (masked later, and always in bounds).  Wave w
+  // fills exactly rows 16w .. 16w+15, the rows it rotates later, so its own
+  // vmcnt wait covers every byte it reads back.
+  //
+  // The loads go through buffer resources whose range ends at the segment's
+  // last token: rows past it read as zero, and no address outside a segment
+  // is touched.  Per-lane byte offsets inside a tile are loop constants
+  // (voff_k / voff_v); lanes that land in LDS row padding get an offset past
+  // any range, so they write zeros there.
+  __device__ __forceinline__ void dma_tile(char* kdst, char* vdst, int s, int n0) {
     const Segment& sg = p.seg[s];
-    const char* kb = static_cast<const char*>(sg.k) + (size_t)head * sg.head * 2;
-    const char* vb = static_cast<const char*>(sg.v) + (size_t)head * sg.head * 2;
     const size_t tok_bytes = (size_t)sg.tok * 2;
-    const int last = sg.count - 1;
-    // Wave w fills exactly rows 16w .. 16w+15 (the rows it rotates later), so
-    // its own vmcnt wait covers every byte it reads back.
+    const size_t off = (size_t)head * sg.head * 2 + (size_t)n0 * tok_bytes;
+    const int nrec = (int)((size_t)(sg.count - n0) * tok_bytes);
+    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<char*>(static_cast<const char*>(sg.k) + off), 0, nrec, kBufferConfig);
+    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<char*>(static_cast<const char*>(sg.v) + off), 0, nrec, kBufferConfig);
     const int wbase = wave * 16 * RBP;
 #pragma unroll
     for (int i = 0; i < DMA_PER_WAVE; ++i) {
-      const int u = i * 64 + lane;                 // 16-byte unit inside the wave's 16 rows
-      const int rr = u / NU, c = u - rr * NU;
-      if (rr < 16 && c < NS) {                     // padding units are never read
-        const int r = wave * 16 + rr;
-        const int nk = min(n0 + key_perm(r), last);
-        const int nv = min(n0 + r, last);
-        __builtin_amdgcn_global_load_lds(kb + (size_t)nk * tok_bytes + c * 16,
-                                         (__attribute__((address_space(3))) void*)(kbuf + buf * TILE + wbase + i * 1024), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(vb + (size_t)nv * tok_bytes + c * 16,
-                                         (__attribute__((address_space(3))) void*)(vbuf + buf * TILE + wbase + i * 1024), 16, 0, 0);
+      if (i * 64 + 64 <= 16 * NU || i * 64 + lane < 16 * NU) {  // the wave's own 16 rows only
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (__attribute__((address_space(3))) void*)(kdst + wbase + i * 1024),
+                                                 16, voff_k[i], 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (__attribute__((address_space(3))) void*)(vdst + wbase + i * 1024),
+                                                 16, voff_v[i], 0, 0, 0);
       }
     }
   }
 
-  // Rotate, in place, the quarter-row of K this lane owns (rows of this wave's own DMA).
-  __device__ __forceinline__ void rotate_tile(int buf, int s, int n0) {
+  // Rotate, in place, the quarter-row of K this lane owns: for every pair,
+  // (x0, x1) -> (x0 c - x1 s, x0 s + x1 c) as two v_dot2 with packed-bf16
+  // (c, -s) and (s, c) from the LDS table.
+  __device__ __forceinline__ void rotate_tile(char* kt, int s, int n0) {
     const Segment& sg = p.seg[s];
     const int n = min(n0 + key_perm(rot_row), sg.count - 1);
     int tt, y, x;
@@ -393,27 +416,27 @@ struct FastAttn {
     const int rw = p.rope_w_off * 8 + x * (B::NPW * 8);
     const int r0 = (b0 == 0 ? rt : (b0 == 1 ? rh : rw)) + c0;
     const int r1 = (b1 == 0 ? rt : (b1 == 1 ? rh : rw)) + c1;
-    char* base = kbuf + buf * TILE + rot_row * RBP + rot_q * SPL * 16;
+    char* base = kt + rot_row * RBP + rot_q * SPL * 16;
 #pragma unroll
     for (int i = 0; i < SPL; ++i) {
-      const int off = 16 * i;
-      uint4 w = *reinterpret_cast<const uint4*>(base + off);
-      uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+      const uint4 w = *reinterpret_cast<const uint4*>(base + 16 * i);
+      const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+      uint32_t out[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int pe = 4 * i + e;
-        const float2 cs = *reinterpret_cast<const float2*>(tab + (pe < esplit ? r0 : r1) + 8 * pe);
-        ws[e] = rotate_pair_bf16(ws[e], cs);
+        const uint2 cs = *reinterpret_cast<const uint2*>(tab + (pe < esplit ? r0 : r1) + 8 * pe);
+        const bf16x2 xv = __builtin_bit_cast(bf16x2, ws[e]);
+        const float y0 = __builtin_amdgcn_fdot2_f32_bf16(xv, __builtin_bit_cast(bf16x2, cs.x), 0.f, false);
+        const float y1 = __builtin_amdgcn_fdot2_f32_bf16(xv, __builtin_bit_cast(bf16x2, cs.y), 0.f, false);
+        out[e] = pack_bf16(y0, y1);
       }
-      *reinterpret_cast<uint4*>(base + off) = make_uint4(ws[0], ws[1], ws[2], ws[3]);
+      *reinterpret_cast<uint4*>(base + 16 * i) = make_uint4(out[0], out[1], out[2], out[3]);
     }
   }
 
-  __device__ __forceinline__ void step(int buf, int n0, int count) {
-    const char* kt = kbuf + buf * TILE;
-    const char* vt = vbuf + buf * TILE;
-    // S^T = K_rot Q_rot^T: [2 key blocks] x [2 query blocks] of 32x32
-    f32x16 sc[2][2];
+  // S^T = K_rot Q_rot^T: [2 query blocks] x [2 key blocks] of 32x32
+  __device__ __forceinline__ void qk(const char* kt, f32x16 (&sc)[2][2]) {
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) { sc[qb][0] = f32x16{}; sc[qb][1] = f32x16{}; }
 #pragma unroll
@@ -427,59 +450,33 @@ struct FastAttn {
         sc[qb][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qreg[qb][c], sc[qb][1], 0, 0, 0);
       }
     }
-    // register r of key block kb holds key kb*32 + (r/8)*16 + hh*8 + r%8
-    float mt[2];
+  }
+
+  // Probabilities p = 2^(s*scale - m_run*scale) of query block qb packed to
+  // bf16 (the PV B operand); returns this lane's partial sum of the packed
+  // values, so the normaliser sums the same rounded weights the PV uses.
+  __device__ __forceinline__ float probs(const f32x16 (&sq)[2], int qb, bf16x8 (&pq)[4]) {
+    const float mb = m_run[qb] * sl2;
+    float acc = 0.f;
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      if (n0 + KT > count) {  // ragged tile (uniform): keys past the segment end score -inf
-        const int lim = count - n0 - hh * 8;
+    for (int kc = 0; kc < 4; ++kc) {
+      uint32_t pw[4];
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r)
-            if (kb * 32 + (r >> 3) * 16 + (r & 7) >= lim) sc[qb][kb][r] = -INFINITY;
+      for (int e = 0; e < 4; ++e) {
+        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sq[kc >> 1][(kc & 1) * 8 + 2 * e], sl2, -mb));
+        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sq[kc >> 1][(kc & 1) * 8 + 2 * e + 1], sl2, -mb));
+        pw[e] = pack_bf16(p0, p1);
+        acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw[e]), kOnes, acc, false);
       }
-      float m = sc[qb][0][0];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) m = fmaxf(m, sc[qb][kb][r]);
-      mt[qb] = fmaxf(m, __shfl_xor(m, 32, 64));
+      pq[kc] = __builtin_bit_cast(bf16x8, make_uint4(pw[0], pw[1], pw[2], pw[3]));
     }
-    if (__any((mt[0] > m_run[0] + tau_raw) | (mt[1] > m_run[1] + tau_raw))) {
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        const float m_new = fmaxf(m_run[qb], mt[qb]);
-        const float alpha = __builtin_amdgcn_exp2f((m_run[qb] - m_new) * sl2);
-        m_run[qb] = m_new;
-        l_run[qb] *= alpha;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) o[qb][db] *= alpha;
-      }
-    }
-    bf16x8 pb[2][4];
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      const float mb = m_run[qb] * sl2;
-      float rs = l_run[qb];
-#pragma unroll
-      for (int kc = 0; kc < 4; ++kc) {
-        uint32_t pw[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[qb][kc >> 1][(kc & 1) * 8 + 2 * e], sl2, -mb));
-          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[qb][kc >> 1][(kc & 1) * 8 + 2 * e + 1], sl2, -mb));
-          pw[e] = pack_bf16(p0, p1);
-          // the normaliser sums the same bf16-rounded weights the PV product uses
-          rs = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw[e]), kOnes, rs, false);
-        }
-        pb[qb][kc] = __builtin_bit_cast(bf16x8, make_uint4(pw[0], pw[1], pw[2], pw[3]));
-      }
-      l_run[qb] = rs;
-    }
-    // O^T += V^T P^T.  Lane (dv = 32db + l32, hh) needs keys 16kc + 8hh + j, j = 0..7:
-    // two transpose reads; in each, lane 4e + q of a 16-lane group points at
-    // row 16kc + 8hh + 4rd + e, dims 32db + 16*(group&1) + 4q .. +3.
+    return acc;
+  }
+
+  // O^T += V^T P^T.  Lane (dv = 32db + l32, hh) needs keys 16kc + 8hh + j, j = 0..7:
+  // two transpose reads; in each, lane 4e + q of a 16-lane group points at
+  // row 16kc + 8hh + 4rd + e, dims 32db + 16*(group&1) + 4q .. +3.
+  __device__ __forceinline__ void pv(const char* vt, const bf16x8 (&pb)[2][4]) {
     const int grp = lane >> 4, i16 = lane & 15;
     const char* vl = vt + (8 * hh + (i16 >> 2)) * RBP + (16 * (grp & 1) + 4 * (i16 & 3)) * 2;
 #pragma unroll
@@ -496,6 +493,64 @@ struct FastAttn {
         for (int qb = 0; qb < 2; ++qb)
           o[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[qb][kc], o[qb][db], 0, 0, 0);
       }
+  }
+
+  // Full tile against the fixed running max, branch-free.  Returns true (for
+  // the whole wave) when some probability reached SUM_LIMIT or is not finite;
+  // the workgroup then recomputes everything with step_exact.
+  __device__ __forceinline__ bool step_fast(const char* kt, const char* vt) {
+    f32x16 sc[2][2];
+    qk(kt, sc);
+    bf16x8 pb[2][4];
+    const float r0 = probs(sc[0], 0, pb[0]);
+    const float r1 = probs(sc[1], 1, pb[1]);
+    l_run[0] += r0;
+    l_run[1] += r1;
+    pv(vt, pb);
+    return __any(!(r0 <= SUM_LIMIT) | !(r1 <= SUM_LIMIT));
+  }
+
+  // Any tile, exact online softmax: keys past `count` are masked, the running
+  // max follows the tile max and O and the normaliser are rescaled.
+  __device__ __forceinline__ void step_exact(const char* kt, const char* vt, int n0, int count) {
+    f32x16 sc[2][2];
+    qk(kt, sc);
+    // register r of key block kb holds key kb*32 + (r/8)*16 + hh*8 + r%8
+    const int lim = count - n0 - hh * 8;
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (kb * 32 + (r >> 3) * 16 + (r & 7) >= lim) sc[qb][kb][r] = -INFINITY;
+    bf16x8 pb[2][4];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      float m = sc[qb][0][0];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) m = fmaxf(m, sc[qb][kb][r]);
+      m = fmaxf(m, __shfl_xor(m, 32, 64));
+      const float m_new = fmaxf(m_run[qb], m);  // finite: every tile has a valid key
+      const float alpha = __builtin_amdgcn_exp2f((m_run[qb] - m_new) * sl2);
+      m_run[qb] = m_new;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) o[qb][db] *= alpha;
+      l_run[qb] = l_run[qb] * alpha + probs(sc[qb], qb, pb[qb]);
+    }
+    pv(vt, pb);
+  }
+
+  __device__ void reset_accumulators() {
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+#pragma unroll
+      for (int i = 0; i < NDB; ++i) o[qb][i] = f32x16{};
+      m_run[qb] = -INFINITY;
+      l_run[qb] = 0.f;
+    }
   }
 
   __device__ void epilogue(int qt) {
@@ -522,53 +577,102 @@ struct FastAttn {
 
 __device__ __forceinline__ void wait_dma() { __builtin_amdgcn_s_waitcnt(0x3f70); }  // vmcnt(0)
 
+// Next full 64-key tile after (s, n0); returns false past the last one.
+__device__ inline bool next_full(const AttnParams& p, int& s, int& n0) {
+  n0 += kKeyTile;
+  if (n0 + kKeyTile > p.seg[s].count) {
+    ++s;
+    n0 = 0;
+    while (s < p.n_seg && p.seg[s].count < kKeyTile) ++s;
+  }
+  return s < p.n_seg;
+}
+
 template <int D, int DT, int DH>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void attn_bf16_fast(const AttnParams p) {
   using F = FastAttn<D, DT, DH>;
-  __shared__ __align__(16) char kbuf[2 * F::TILE];
-  __shared__ __align__(16) char vbuf[2 * F::TILE];
+  // Two K and two V tiles as distinct objects: the compiler can then tell the
+  // DMA into one buffer from the reads of the other and does not wait on it.
+  __shared__ __align__(16) char k0[F::TILE];
+  __shared__ __align__(16) char k1[F::TILE];
+  __shared__ __align__(16) char v0[F::TILE];
+  __shared__ __align__(16) char v1[F::TILE];
   extern __shared__ __align__(16) char rope_lds[];
 
   int head, qt;
   if (!map_workgroup(p, head, qt)) return;
 
-  // cos/sin table -> LDS (read by the key rotation of every tile)
+  // packed-bf16 rotation table -> LDS (read by the key rotation of every tile)
   {
     const int n16 = (p.rope_bytes + 15) >> 4;
-    const uint4* src = reinterpret_cast<const uint4*>(p.rope);
+    const uint4* src = reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(p.rope) + p.rope_bytes);
     for (int i = threadIdx.x; i < n16; i += 256) reinterpret_cast<uint4*>(rope_lds)[i] = src[i];
   }
-  F a(p, kbuf, vbuf, rope_lds, head);
-  int s = 0, n0 = 0;
-  while (s < p.n_seg && p.seg[s].count == 0) ++s;
-  if (s < p.n_seg) a.dma_tile(0, s, n0);
+  F a(p, rope_lds, head);
+  // Full 64-key tiles go through the pipelined fast loop; the ragged last tile
+  // of each segment (and, after an overflow, everything) through exact steps.
+  // Tile order does not change the softmax result.
+  __shared__ int ovf[2][4];  // per-wave overflow flags, one set per unrolled half
+  int s = 0;
+  while (s < p.n_seg && p.seg[s].count < F::KT) ++s;
+  const bool have_full = s < p.n_seg;
+  if (have_full) a.dma_tile(k0, v0, s, 0);
   a.init_queries(qt);
   wait_dma();
-  __syncthreads();  // the table is in LDS
-  if (s < p.n_seg) a.rotate_tile(0, s, n0);
-  __syncthreads();
-
-  int buf = 0;
-  while (s < p.n_seg) {
-    int s1 = s, n1 = n0 + F::KT;
-    if (n1 >= p.seg[s1].count) {
-      ++s1;
-      n1 = 0;
-      while (s1 < p.n_seg && p.seg[s1].count == 0) ++s1;
-    }
-    // past the last tile, the current one is loaded again into the idle buffer (never read)
-    const bool has_next = s1 < p.n_seg;
-    const int sl = has_next ? s1 : s, nl = has_next ? n1 : n0;
-    a.dma_tile(buf ^ 1, sl, nl);
-    const int count = p.seg[s].count;
-    a.step(buf, n0, count);
-    wait_dma();
-    a.rotate_tile(buf ^ 1, sl, nl);
+  __syncthreads();  // the table and the first tile are in LDS
+  bool overflow = false;
+  if (have_full) {
+    a.rotate_tile(k0, s, 0);
     __syncthreads();
-    buf ^= 1;
-    s = s1;
-    n0 = n1;
+    int s1 = s, n1 = 0;
+    bool more = next_full(p, s1, n1);
+    if (more) a.dma_tile(k1, v1, s1, n1);
+    a.step_exact(k0, v0, 0, p.seg[s].count);  // sets the running max
+    if (more) {
+      wait_dma();
+      a.rotate_tile(k1, s1, n1);
+      __syncthreads();
+      more = next_full(p, s1, n1);
+      while (true) {
+        if (more) a.dma_tile(k0, v0, s1, n1);
+        ovf[0][a.wave] = a.step_fast(k1, v1);
+        if (more) {
+          wait_dma();
+          a.rotate_tile(k0, s1, n1);
+        }
+        __syncthreads();
+        if (ovf[0][0] | ovf[0][1] | ovf[0][2] | ovf[0][3]) { overflow = true; break; }
+        if (!more) break;
+        more = next_full(p, s1, n1);
+
+        if (more) a.dma_tile(k1, v1, s1, n1);
+        ovf[1][a.wave] = a.step_fast(k0, v0);
+        if (more) {
+          wait_dma();
+          a.rotate_tile(k1, s1, n1);
+        }
+        __syncthreads();
+        if (ovf[1][0] | ovf[1][1] | ovf[1][2] | ovf[1][3]) { overflow = true; break; }
+        if (!more) break;
+        more = next_full(p, s1, n1);
+      }
+    }
+    __syncthreads();
+  }
+  // Exact, single-buffered passes: the ragged tiles, or every tile again after
+  // an overflow (rare: a score more than 14 powers of two above the first tile's max).
+  if (overflow) a.reset_accumulators();
+  for (int ss = 0; ss < p.n_seg; ++ss) {
+    const int cnt = p.seg[ss].count;
+    for (int nn = overflow ? 0 : cnt - cnt % F::KT; nn < cnt; nn += F::KT) {
+      a.dma_tile(k0, v0, ss, nn);
+      wait_dma();
+      a.rotate_tile(k0, ss, nn);
+      __syncthreads();
+      a.step_exact(k0, v0, nn, cnt);
+      __syncthreads();
+    }
   }
   a.epilogue(qt);
 }
@@ -665,7 +769,14 @@ hipError_t launch_attention(const AttnParams& p_in, int dtype, int head_dim, hip
   AttnParams p = p_in;
   const int heads_per_xcd = (p.n_heads + 7) / 8;
   if (dtype == 0) {  // bf16
-    const bool wan = p.np_h == p.np_w && p.np_h == head_dim / 6 && p.rope_bytes <= kMaxRopeLdsBytes;
+    // the fast kernel's buffer ranges are 31-bit byte counts
+    size_t max_seg_bytes = 0;
+    for (int i = 0; i < p.n_seg; ++i) {
+      const size_t b = (size_t)p.seg[i].count * p.seg[i].tok * 2;
+      if (b > max_seg_bytes) max_seg_bytes = b;
+    }
+    const bool wan = p.np_h == p.np_w && p.np_h == head_dim / 6 && p.rope_bytes <= kMaxRopeLdsBytes &&
+                     max_seg_bytes < (size_t)kOutOfRange;
     if (wan && (head_dim == 128 || head_dim == 64)) {
       p.n_qtiles = (p.n_q + 255) / 256;
       const dim3 grid(8 * heads_per_xcd * p.n_qtiles);

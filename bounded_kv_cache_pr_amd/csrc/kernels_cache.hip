@@ -1,5 +1,5 @@
 // Cache-maintenance kernels of the PR-Sink path on gfx950:
-//   kv_write     raw K/V [T][H][d] -> slot layout [H][t_pad][d]
+//   kv_write     raw K/V [T][H][d] -> slot layout [t_pad][H][d] (contiguous copy)
 //   slot_copy    whole block slot (all layers) -> another slot; source and
 //                destination come from device state, so no host round trip
 //   retrieve     fingerprint l2-normalisation + argmax over the bank (fp64)
@@ -10,26 +10,21 @@ namespace prsink {
 namespace {
 
 // ---------------------------------------------------------------------------
-// kv_write: raw K and V [T][H][d] -> slot layout [H][t_pad][d], optionally to
-// a second destination.  Each thread moves 16-byte chunks; rows past T (the
-// slot's padding) are never written, so they stay zero.
+// kv_write: raw K and V [T][H][d] -> slot layout [t_pad][H][d] (the same
+// token-major order, so a contiguous copy), optionally to a second
+// destination.  Rows past T (the slot's padding) are never written and stay
+// zero.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void kv_write_kernel(
     const uint4* __restrict__ k_src, const uint4* __restrict__ v_src, uint4* __restrict__ k_dst0,
     uint4* __restrict__ v_dst0, uint4* __restrict__ k_dst1, uint4* __restrict__ v_dst1,
-    int n_tok, int n_heads, int row_chunks, int t_pad) {
-  const size_t total = (size_t)n_tok * n_heads * row_chunks;
+    size_t n_chunks) {
   const size_t stride = (size_t)gridDim.x * blockDim.x;
-  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += stride) {
-    const size_t row = i / row_chunks;              // (token, head) row of the source
-    const int c = (int)(i - row * row_chunks);
-    const int h = (int)(row % n_heads);
-    const size_t n = row / n_heads;
-    const size_t dst = ((size_t)h * t_pad + n) * row_chunks + c;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n_chunks; i += stride) {
     const uint4 kv = k_src[i], vv = v_src[i];
-    k_dst0[dst] = kv;
-    v_dst0[dst] = vv;
-    if (k_dst1) { k_dst1[dst] = kv; v_dst1[dst] = vv; }
+    k_dst0[i] = kv;
+    v_dst0[i] = vv;
+    if (k_dst1) { k_dst1[i] = kv; v_dst1[i] = vv; }
   }
 }
 
@@ -185,15 +180,14 @@ __global__ void state_init_kernel(DevState* st) {
 hipError_t launch_kv_write(const void* k_src, const void* v_src, void* k_dst0, void* v_dst0,
                            void* k_dst1, void* v_dst1, int n_tok, int n_heads, int head_dim,
                            int t_pad, int elem_bytes, hipStream_t s) {
-  const int row_chunks = head_dim * elem_bytes / 16;
-  const size_t total = (size_t)n_tok * n_heads * row_chunks;
-  size_t blocks = (total + 255) / 256;
+  (void)t_pad;
+  const size_t n_chunks = (size_t)n_tok * n_heads * head_dim * elem_bytes / 16;
+  size_t blocks = (n_chunks + 255) / 256;
   if (blocks > 256 * 8) blocks = 256 * 8;
   hipLaunchKernelGGL(kv_write_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
                      static_cast<const uint4*>(k_src), static_cast<const uint4*>(v_src),
                      static_cast<uint4*>(k_dst0), static_cast<uint4*>(v_dst0),
-                     static_cast<uint4*>(k_dst1), static_cast<uint4*>(v_dst1), n_tok, n_heads,
-                     row_chunks, t_pad);
+                     static_cast<uint4*>(k_dst1), static_cast<uint4*>(v_dst1), n_chunks);
   return hipGetLastError();
 }
 

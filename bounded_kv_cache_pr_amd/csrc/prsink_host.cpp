@@ -65,7 +65,8 @@ bool magic_exact(uint32_t d, uint32_t n_max) {
 // Arena layout (offsets in bytes from the arena base):
 //   [state | fingerprints | rope table] [Ref slot] [block slots...]
 // Block slots: Static, Dynamic, window 0..W-1, bank 0..M-1.  Each slot holds,
-// per layer, K [H][t_pad][d] then V [H][t_pad][d].
+// per layer, K [t_pad][H][d] then V [t_pad][H][d] (token-major, like the tensors the
+// caller passes, so every segment shares one row stride; rows past T stay zero).
 struct Layout {
   int elem, tpf, tb, tr, tb_pad, tr_pad;
   size_t kv_b, layer_b, slot_b;   // block slot: one tensor, one layer, whole slot
@@ -134,8 +135,8 @@ Layout make_layout(const pr_sink_config* c) {
   off = align_up(off + sizeof(double) * c->bank_size * c->fp_dim, 256);
   L.off_phi_cur = off;
   off = align_up(off + sizeof(double) * c->fp_dim, 256);
-  L.off_rope = off;
-  off = align_up(off + sizeof(float) * 2 * L.rope_entries, kAlign);
+  L.off_rope = off;  // fp32 (cos, sin) table, then the packed-bf16 rotation table
+  off = align_up(off + 16 * (size_t)L.rope_entries, kAlign);
   L.off_ref = off;
   off += L.slot_r;
   L.off_blocks = off;
@@ -144,17 +145,32 @@ Layout make_layout(const pr_sink_config* c) {
   return L;
 }
 
-// cos/sin of every (band, position, pair), computed in double, stored as float.
-std::vector<float> rope_table(const pr_sink_config* c, const Layout& L) {
-  std::vector<float> t(2 * (size_t)L.rope_entries);
+// bf16 bits of a float, round to nearest even.
+uint32_t bf16_bits(float f) {
+  uint32_t u;
+  std::memcpy(&u, &f, 4);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// cos/sin of every (band, position, pair), computed in double.  Two tables of
+// rope_entries 8-byte entries each: fp32 (cos, sin), then the same angles as
+// packed bf16 pairs (cos, -sin) and (sin, cos), the operands of the two
+// v_dot2 products that rotate one bf16 key pair.
+std::vector<uint32_t> rope_table(const pr_sink_config* c, const Layout& L) {
+  const size_t E = (size_t)L.rope_entries;
+  std::vector<uint32_t> t(4 * E);
   auto fill = [&](int base, int npos, int pos0, int band_dim) {
     const int np = band_dim / 2;
     for (int ps = 0; ps < npos; ++ps)
       for (int i = 0; i < np; ++i) {
         const double w = std::pow(c->rope_theta, -2.0 * i / band_dim);
         const double a = (double)(pos0 + ps) * w;
-        t[2 * (size_t)(base + ps * np + i)] = (float)std::cos(a);
-        t[2 * (size_t)(base + ps * np + i) + 1] = (float)std::sin(a);
+        const float cs = (float)std::cos(a), sn = (float)std::sin(a);
+        const size_t e = (size_t)(base + ps * np + i);
+        std::memcpy(&t[2 * e], &cs, 4);
+        std::memcpy(&t[2 * e + 1], &sn, 4);
+        t[2 * E + 2 * e] = bf16_bits(cs) | (bf16_bits(-sn) << 16);
+        t[2 * E + 2 * e + 1] = bf16_bits(sn) | (bf16_bits(cs) << 16);
       }
   };
   fill(0, L.n_t, c->t0, c->rope_dims[0]);
@@ -251,8 +267,8 @@ int pr_sink_cache_init(const pr_sink_config* cfg, void* arena_dev, size_t arena_
     hipStream_t s = as_stream(stream);
     char* a = static_cast<char*>(arena_dev);
     PRS_HIP(hipMemsetAsync(a, 0, L.total, s));  // zero padding keeps masked keys finite
-    std::vector<float> tab = rope_table(cfg, L);
-    PRS_HIP(hipMemcpyAsync(a + L.off_rope, tab.data(), tab.size() * sizeof(float),
+    std::vector<uint32_t> tab = rope_table(cfg, L);
+    PRS_HIP(hipMemcpyAsync(a + L.off_rope, tab.data(), tab.size() * sizeof(uint32_t),
                            hipMemcpyHostToDevice, s));
     PRS_HIP(launch_state_init(reinterpret_cast<DevState*>(a + L.off_state), s));
     PRS_HIP(hipStreamSynchronize(s));
@@ -336,8 +352,9 @@ int pr_sink_attend(pr_sink_cache* c, int32_t layer, const void* q_raw, const voi
     const char* kb = slot_base + (size_t)layer * layer_bytes;
     sg.k = kb;
     sg.v = kb + kv_bytes;
-    sg.tok = D;
-    sg.head = (int64_t)t_pad * D;
+    sg.tok = (int64_t)g.n_heads * D;
+    sg.head = D;
+    (void)t_pad;
   };
   const int b = c->next_block;
   for (int s = 0; s < n_seg; ++s) {

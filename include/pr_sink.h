@@ -167,8 +167,8 @@ int pr_sink_bank_state(pr_sink_cache* c, int32_t* ids_host, double* fp_host,
                        int32_t* misc_host, void* stream);
 
 /* Device pointers to the raw K and V of one slot and layer, for inspection.
- * Both are [H][t_pad][d]; t_pad (tokens per head, a multiple of 64; the
- * padding rows are zero) goes to *t_pad_out. */
+ * Both are [t_pad][H][d], token-major like the tensors passed in; t_pad (a
+ * multiple of 64; the padding rows are zero) goes to *t_pad_out. */
 int pr_sink_slot_view(const pr_sink_cache* c, int32_t slot, int32_t layer, void** k_dev,
                       void** v_dev, int32_t* t_pad_out);
 
