@@ -69,7 +69,8 @@ def lib() -> ctypes.CDLL:
             "pr_sink_clean_kv_write": (i32, [vp, i32, vp, vp, vp]),
             "pr_sink_bank_update": (i32, [vp, i32, vp]),
             "pr_sink_bank_state": (i32, [vp, vp, vp, vp, vp]),
-            "pr_sink_slot_view": (i32, [vp, i32, i32, POINTER(vp), POINTER(vp), POINTER(i32)]),
+            "pr_sink_slot_view": (i32, [vp, i32, i32, POINTER(vp), POINTER(vp), POINTER(vp),
+                                        POINTER(i32)]),
             "pr_sink_segments": (i32, [vp, vp, vp, POINTER(i32)]),
             "pr_sink_cache_destroy": (i32, [vp]),
             "pr_sink_last_error": (ctypes.c_char_p, []),
@@ -208,17 +209,23 @@ class PRSinkCache:
         check(lib().pr_sink_segments(self._h, tok.ctypes.data, ts.ctypes.data, byref(n)))
         return [(int(tok[i]), int(ts[i])) for i in range(n.value)]
 
-    def slot_view(self, slot: int, layer: int):
-        """Torch views of one slot's raw K and V, both [t_pad][H][d]."""
-        k, v, tp = c_void_p(), c_void_p(), c_int32()
-        check(lib().pr_sink_slot_view(self._h, slot, layer, byref(k), byref(v), byref(tp)))
+    def slot_view(self, slot: int, layer: int, rotated: bool = False):
+        """Torch views of one slot's raw K and V, [t_pad][H][d] each; with
+        rotated=True also its rotated K."""
+        k, v, r, tp = c_void_p(), c_void_p(), c_void_p(), c_int32()
+        check(lib().pr_sink_slot_view(self._h, slot, layer, byref(k), byref(v), byref(r), byref(tp)))
         c = self.cfg
         n = c.n_heads * tp.value * c.head_dim
         esz = 2 if c.dtype == DTYPE_BF16 else 4
         base = self.arena.data_ptr()
-        kt = self.arena[k.value - base:k.value - base + n * esz].view(self.torch_dtype)
-        vt = self.arena[v.value - base:v.value - base + n * esz].view(self.torch_dtype)
-        return (kt.view(tp.value, c.n_heads, c.head_dim), vt.view(tp.value, c.n_heads, c.head_dim))
+
+        def view(ptr):
+            t = self.arena[ptr - base:ptr - base + n * esz].view(self.torch_dtype)
+            return t.view(tp.value, c.n_heads, c.head_dim)
+
+        if rotated:
+            return view(k.value), view(v.value), view(r.value)
+        return view(k.value), view(v.value)
 
     def slot_index_bank(self, i: int) -> int:
         return SLOT_WINDOW0 + self.cfg.window_slots + i

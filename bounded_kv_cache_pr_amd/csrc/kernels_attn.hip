@@ -1,22 +1,33 @@
-// PR-Sink block-causal attention with RoPE follow on gfx950.
+// PR-Sink block-causal attention on gfx950.
 //
 // The current block's queries attend over [Ref; Static; Dynamic; window;
 // current] with scale 1/sqrt(d) (LiveAnimate review on paper.rainbus.top,
-// full-pipeline paragraph, attention formula and the prose around it: the
-// current block is attended too).  Every key is read raw and rotated with 3D
-// RoPE at its segment's *current* temporal slot and its latent (row, column)
-// before use (same paragraph: raw keys re-rotated at the current cache
-// position; novelty paragraph: reuse decoupled from the original timestamp).
+// full-pipeline paragraph: the attention formula and the prose around it,
+// which includes the current block).  Keys arrive already rotated at their
+// segment's current position (RoPE follow runs when a block takes a place in
+// the cache, in rope_follow); the queries are rotated here, at the current
+// block's positions.
 //
-// Common structure of the bf16 kernels:
-//   * S^T = K_rot Q_rot^T on v_mfma_f32_32x32x16_bf16.  A lane owns one query
-//     column and 16 key rows of each 32x32 block, so the softmax row max/sum
-//     stay in-lane except for one exchange with lane ^ 32.  Keys sit in LDS
-//     with bits 2 and 3 of their row index swapped, which makes the
-//     probabilities a lane holds after QK^T exactly the B operand of the PV
-//     MFMA, with no shuffles.
-//   * O^T = V^T P^T accumulates in fp32; the online softmax runs in base 2
-//     with the 1/sqrt(d) scale folded into one FMA per score.
+// bf16 kernel, one workgroup = 256 query rows of one head, 4 waves x 64 rows:
+//   * S'^T = K_rot Q'^T on v_mfma_f32_32x32x16_bf16, with
+//     Q' = bf16(Q_rot * log2(e) / sqrt(d)), so scores come out in base 2.  A
+//     lane owns one query column and 16 key rows of each 32x32 block, so the
+//     softmax needs no shuffles except one exchange with lane ^ 32.  Keys sit
+//     in LDS with bits 2 and 3 of their row index swapped: the probabilities
+//     a lane holds after QK^T are then exactly the B operand of the PV MFMA.
+//   * O^T = V^T P^T accumulates in fp32.  V stays row-major in LDS; the V^T
+//     operand comes from ds_read_b64_tr_b16.
+//   * Softmax against a fixed reference: the first 64-key tile sets each row's
+//     max m; every later score is accumulated as 2^(s' - m), with -m folded
+//     into the accumulator the QK^T MFMA starts from.  Probabilities above 1
+//     are harmless in fp32; if a row's sum ever leaves [0, 2^64] (a score more
+//     than 64 powers of two above the first tile's max) the workgroup redoes
+//     the whole row block with exact online softmax.
+//   * Tiles move global -> LDS by DMA (buffer_load ... lds) into a 3-stage
+//     ring, two tiles ahead.  Iteration j computes QK^T of tile j+1 and PV of
+//     tile j, so the exp2 of one tile overlaps the MFMAs of its neighbours.
+//   * Ragged tiles (the last of each segment) run afterwards through the exact
+//     online-softmax step with masking; tile order does not change the result.
 // The fp32 kernel is a plain one-query-per-lane loop for fp32 caches.
 #include "prsink_internal.h"
 
@@ -27,6 +38,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) char lds_char;
 
 __device__ constexpr bf16x2 kOnes = {(__bf16)1.0f, (__bf16)1.0f};
 
@@ -40,59 +52,8 @@ __device__ inline uint32_t pack_bf16(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
-// One RoPE pair stored as two bf16 in a dword (element 0 in the low half).
-__device__ inline uint32_t rotate_pair_bf16(uint32_t w, float2 cs) {
-  const float x0 = __uint_as_float(w << 16);
-  const float x1 = __uint_as_float(w & 0xffff0000u);
-  return pack_bf16(x0 * cs.x - x1 * cs.y, x0 * cs.y + x1 * cs.x);
-}
-
-// n / d for the token ranges the host checked: multiply-high, or n itself when d == 1.
-__device__ inline uint32_t div_magic(uint32_t n, uint32_t magic, uint32_t one) {
-  return __umulhi(n, magic) + n * one;
-}
-
-// Where the cos/sin of RoPE pair `pair` live: band base offset, row stride
-// (pairs per band) and which position component (0 t, 1 h, 2 w) indexes it.
-struct PairTab {
-  int base, stride, comp;
-};
-
-__device__ inline PairTab pair_tab(const AttnParams& p, int pair) {
-  PairTab t;
-  if (pair < p.np_t) {
-    t.base = pair; t.stride = p.np_t; t.comp = 0;
-  } else if (pair < p.np_t + p.np_h) {
-    t.base = p.rope_h_off + pair - p.np_t; t.stride = p.np_h; t.comp = 1;
-  } else {
-    t.base = p.rope_w_off + pair - p.np_t - p.np_h; t.stride = p.np_w; t.comp = 2;
-  }
-  return t;
-}
-
-__device__ inline float2 pair_cs(const AttnParams& p, const PairTab& t, int tt, int y, int x) {
-  const int pos = t.comp == 0 ? tt : (t.comp == 1 ? y : x);
-  return p.rope[t.base + pos * t.stride];
-}
-
-__device__ inline void token_pos(const AttnParams& p, int n, int t_index, int& tt, int& y, int& x) {
-  const int f = div_magic(n, p.magic_hw, p.one_hw), j = n - f * p.hw;
-  y = div_magic(j, p.magic_w, p.one_w);
-  x = j - y * p.lat_w;
-  tt = t_index + f;
-}
-
 // Row r of a 64-row key tile lives at LDS row key_perm(r): bits 2 and 3 swapped.
 __device__ inline int key_perm(int r) { return (r & ~0xC) | ((r & 4) << 1) | ((r & 8) >> 1); }
-
-// Rotates 8 raw bf16 (4 pairs, starting at pair `pair0`) of one row at (tt, y, x).
-__device__ inline bf16x8 rotate_chunk_generic(const AttnParams& p, uint4 w, int pair0, int tt,
-                                              int y, int x) {
-  uint32_t ws[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-  for (int e = 0; e < 4; ++e) ws[e] = rotate_pair_bf16(ws[e], pair_cs(p, pair_tab(p, pair0 + e), tt, y, x));
-  return __builtin_bit_cast(bf16x8, make_uint4(ws[0], ws[1], ws[2], ws[3]));
-}
 
 // XCD-aware tile order: consecutive workgroup ids land on different XCDs, so
 // every XCD gets whole heads; the query tiles of a head then share that XCD's
@@ -105,265 +66,123 @@ __device__ inline bool map_workgroup(const AttnParams& p, int& head, int& qt) {
   return head < p.n_heads;
 }
 
-// ---------------------------------------------------------------------------
-// Generic bf16 kernel (any RoPE band split): 4 waves x 32 query rows, one
-// 64-key tile staged per iteration through registers.
-// ---------------------------------------------------------------------------
-template <int D>
-__global__ __launch_bounds__(256) void attn_bf16_generic(const AttnParams p) {
-  constexpr int KT = kKeyTile;
-  constexpr int QT = 128;
-  constexpr int KS = D + 8;         // LDS K row stride (bf16 elements)
-  constexpr int VS = KT + 8;        // LDS V^T row stride
-  constexpr int NC = D / 16;
-  constexpr int NDB = D / 32;
-  __shared__ __align__(16) uint16_t Ks[KT * KS];
-  __shared__ __align__(16) uint16_t Vs[D * VS];
-
-  int head, qt;
-  if (!map_workgroup(p, head, qt)) return;
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int hh = lane >> 5, l32 = lane & 31;
-  const int H = p.n_heads;
-
-  const int qrow = qt * QT + wave * 32 + l32;
-  const bool qvalid = qrow < p.n_q;
-  bf16x8 qreg[NC];
-  {
-    int tq = 0, yq = 0, xq = 0;
-    if (qvalid) token_pos(p, qrow, p.q_t_index, tq, yq, xq);
-    const uint16_t* qp = static_cast<const uint16_t*>(p.q) + ((size_t)qrow * H + head) * D;
-#pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      const int off = 16 * c + 8 * hh;
-      const uint4 w = qvalid ? *reinterpret_cast<const uint4*>(qp + off) : make_uint4(0, 0, 0, 0);
-      qreg[c] = rotate_chunk_generic(p, w, off / 2, tq, yq, xq);
-    }
-  }
-
-  constexpr int KCPR = D / 8;             // 16-byte chunks per key row
-  constexpr int KROWS = 256 / KCPR;
-  const int kcc = tid % KCPR;
-  const int kr0 = tid / KCPR;
-
-  f32x16 o[NDB];
-#pragma unroll
-  for (int i = 0; i < NDB; ++i) o[i] = f32x16{};
-  float m_run = -INFINITY, l_run = 0.f;
-  const float sl2 = p.scale_log2;
-
-  for (int s = 0; s < p.n_seg; ++s) {
-    const Segment sg = p.seg[s];
-    const int count = sg.count;
-    const uint16_t* kbase = static_cast<const uint16_t*>(sg.k) + (size_t)head * sg.head;
-    const uint16_t* vbase = static_cast<const uint16_t*>(sg.v) + (size_t)head * sg.head;
-    for (int n0 = 0; n0 < count; n0 += KT) {
-#pragma unroll
-      for (int it = 0; it < KT / KROWS; ++it) {
-        const int r = kr0 + it * KROWS;
-        const int n = n0 + r;
-        uint4 w = make_uint4(0, 0, 0, 0);
-        if (n < count) {
-          int tt, y, x;
-          token_pos(p, n, sg.t_index, tt, y, x);
-          w = __builtin_bit_cast(uint4, rotate_chunk_generic(
-              p, *reinterpret_cast<const uint4*>(kbase + (size_t)n * sg.tok + kcc * 8), kcc * 4, tt, y, x));
-        }
-        *reinterpret_cast<uint4*>(&Ks[key_perm(r) * KS + kcc * 8]) = w;
-      }
-      {  // V rows -> V^T in LDS
-        const int key = tid % KT, cg = tid / KT;
-        const int n = n0 + key;
-#pragma unroll
-        for (int it = 0; it < D / 32; ++it) {
-          const int ch = cg + 4 * it;
-          uint4 w = make_uint4(0, 0, 0, 0);
-          if (n < count) w = *reinterpret_cast<const uint4*>(vbase + (size_t)n * sg.tok + ch * 8);
-          const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            Vs[(ch * 8 + 2 * e) * VS + key] = (uint16_t)(ws[e] & 0xffffu);
-            Vs[(ch * 8 + 2 * e + 1) * VS + key] = (uint16_t)(ws[e] >> 16);
-          }
-        }
-      }
-      __syncthreads();
-
-      f32x16 sc[2];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        sc[kb] = f32x16{};
-#pragma unroll
-        for (int c = 0; c < NC; ++c) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(&Ks[(kb * 32 + l32) * KS + c * 16 + hh * 8]);
-          sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[c], sc[kb], 0, 0, 0);
-        }
-      }
-      // register r of block kb holds key kb*32 + (r/8)*16 + hh*8 + r%8
-      float mt = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = n0 + kb * 32 + (r >> 3) * 16 + hh * 8 + (r & 7);
-          const float v = key < count ? sc[kb][r] * sl2 : -INFINITY;
-          sc[kb][r] = v;
-          mt = fmaxf(mt, v);
-        }
-      mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-      const float m_new = fmaxf(m_run, mt);  // finite: every tile has a valid key
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-      m_run = m_new;
-      float rs = 0.f;
-      bf16x8 pb[4];
-#pragma unroll
-      for (int kc = 0; kc < 4; ++kc) {
-        uint32_t pw[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float p0 = __builtin_amdgcn_exp2f(sc[kc >> 1][(kc & 1) * 8 + 2 * e] - m_new);
-          const float p1 = __builtin_amdgcn_exp2f(sc[kc >> 1][(kc & 1) * 8 + 2 * e + 1] - m_new);
-          rs += p0 + p1;
-          pw[e] = pack_bf16(p0, p1);
-        }
-        pb[kc] = __builtin_bit_cast(bf16x8, make_uint4(pw[0], pw[1], pw[2], pw[3]));
-      }
-      l_run = l_run * alpha + rs;
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) o[db] *= alpha;
-#pragma unroll
-      for (int db = 0; db < NDB; ++db)
-#pragma unroll
-        for (int kc = 0; kc < 4; ++kc) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(&Vs[(db * 32 + l32) * VS + kc * 16 + hh * 8]);
-          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kc], o[db], 0, 0, 0);
-        }
-      __syncthreads();
-    }
-  }
-
-  // register 4g+e of block db is dv = 32db + 8g + 4hh + e
-  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
-  const float inv = 1.0f / l_tot;
-  if (qvalid) {
-    uint16_t* op = static_cast<uint16_t*>(p.out) + ((size_t)qrow * H + head) * D;
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const uint2 w = make_uint2(pack_bf16(o[db][4 * g] * inv, o[db][4 * g + 1] * inv),
-                                   pack_bf16(o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv));
-        *reinterpret_cast<uint2*>(op + db * 32 + g * 8 + hh * 4) = w;
-      }
-  }
+__device__ inline uint32_t lds_addr(const char* p) {
+  return (uint32_t)(uintptr_t)(const lds_char*)p;
 }
 
-// ---------------------------------------------------------------------------
-// Fast bf16 kernel for the Wan-style band split (t = d - 4*floor(d/6), h = w =
-// 2*floor(d/6)), the layout of every workload here.
-//   * 4 waves x 64 query rows (two 32-row MFMA column blocks per wave): every
-//     K and V operand read from LDS feeds two MFMAs.
-//   * K and V tiles move global -> LDS by DMA (global_load_lds_dwordx4), no
-//     registers in between.  LDS rows are padded (d=128: 304-byte stride, so
-//     16 consecutive rows start 12 banks apart and the 16-byte operand reads
-//     of a 16-lane phase cover all 64 banks once); every LDS address is then
-//     a per-lane base plus an immediate.  DMA lanes that land in padding are
-//     masked off.  The DMA for tile i+1 is issued before tile i is computed
-//     (double-buffered LDS).
-//   * Each wave rotates, in place, the 16 key rows its own DMA brought in
-//     (RoPE follow), with cos/sin read from an LDS copy of the table.
-//   * V stays row-major; the PV operand (V^T) comes from ds_read_b64_tr_b16,
-//     which returns, within each 16-lane group, lane i element e = the value
-//     lane 4e + i/4 points at, element i%4.
-//   * Ragged tiles (the last of each segment) mask keys past the end in a
-//     short uniform branch; the rest of the step is shared.
-//   * Online softmax rescales lazily: the running max used for exp2 moves
-//     only when a score exceeds it by more than 2^8, so probabilities stay
-//     <= 256 and the O rescale is skipped on most tiles.
-// ---------------------------------------------------------------------------
-template <int D, int DT, int DH>
-struct Bands {
-  static constexpr int NPT = DT / 2, NPH = DH / 2, NPW = (D - DT - DH) / 2;
-  static constexpr int band(int g) { return g < NPT ? 0 : (g < NPT + NPH ? 1 : 2); }
-  static constexpr int start(int b) { return b == 0 ? 0 : (b == 1 ? NPT : NPT + NPH); }
+// 16 bytes per lane from a buffer resource into LDS: lane i writes
+// M0 + 16 i.  The load is invisible to the compiler's counters; callers wait
+// on vmcnt themselves.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t lds, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :: "s"(lds), "v"(voff), "s"(r) : "memory", "m0");
+}
+
+// s_waitcnt vmcnt(n), other counters untouched (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt(0x3f70 | (N & 15) | ((N >> 4) << 14));
+}
+
+// Walks the full 64-key tiles in segment order.
+struct TileCursor {
+  int s, n0;
+  __device__ void first(const AttnParams& p) {
+    s = 0;
+    n0 = 0;
+    while (s < p.n_seg && p.seg[s].count < kKeyTile) ++s;
+  }
+  __device__ void next(const AttnParams& p) {
+    n0 += kKeyTile;
+    if (s < p.n_seg && n0 + kKeyTile > p.seg[s].count) {
+      ++s;
+      n0 = 0;
+      while (s < p.n_seg && p.seg[s].count < kKeyTile) ++s;
+    }
+  }
 };
 
-template <int D, int DT, int DH>
-struct FastAttn {
-  using B = Bands<D, DT, DH>;
+template <int D>
+struct Attn {
   static constexpr int KT = kKeyTile;    // keys per tile
   static constexpr int QT = 256;         // query rows per workgroup
   static constexpr int RB = D * 2;       // bytes per key row
-  static constexpr int NS = RB / 16;     // 16-byte slots per row
-  static constexpr int RBP = D == 128 ? RB + 48 : RB + 16;  // padded LDS row stride
+  static constexpr int NS = RB / 16;     // 16-byte data units per row
+  // Padded LDS row stride: 16 consecutive rows start 12 (d=128) or 36 (d=64)
+  // banks apart, so the 16-byte operand reads of a 16-lane phase cover all 64
+  // banks once.
+  static constexpr int RBP = D == 128 ? RB + 48 : RB + 16;
   static constexpr int NU = RBP / 16;    // 16-byte units per padded row
-  static constexpr int TILE = KT * RBP;  // bytes per K or V tile in LDS
-  static constexpr int DMA_PER_WAVE = (16 * NU + 63) / 64;  // 1 KB DMA instructions per wave per tensor
+  static constexpr int NDMA = (KT * NU + 255) / 256;  // DMA instructions per wave, tile and tensor
+  static constexpr int TILE = NDMA * 4 * 1024;        // bytes per tile buffer (tail slack included)
+  static constexpr int STAGES = 3;
   static constexpr int NC = D / 16;      // QK^T k-steps
   static constexpr int NDB = D / 32;     // dv blocks
-  static constexpr int SPL = NS / 4;     // slots each lane rotates (a quarter of a row)
-  static constexpr int PPL = SPL * 4;    // RoPE pairs each lane rotates
-  // A tile whose partial row sum of probabilities exceeds this takes the slow
-  // path (exact tile max, rescale).  Below it every probability is < 2^14.
-  static constexpr float SUM_LIMIT = 16384.0f;
+  static constexpr float SUM_LIMIT = 18446744073709551616.0f;  // 2^64
 
   const AttnParams& p;
-  const char* tab;  // LDS: packed-bf16 rotation table
-  int head, tid, lane, wave, hh, l32;
-  float sl2;
-  // rotation: this lane's row inside its wave's 16 rows, and the band pattern of its pairs
-  int rot_row, rot_q, b0, b1, esplit, c0, c1;
+  char* smem;  // K stages then V stages
+  int head, lane, wave, hh, l32;
+  uint32_t tok_bytes;
 
-  uint32_t voff_k[DMA_PER_WAVE], voff_v[DMA_PER_WAVE];
+  uint32_t voff_k[NDMA], voff_v[NDMA];
 
   bf16x8 qreg[2][NC];
   f32x16 o[2][NDB];
   float m_run[2], l_run[2];
 
-  __device__ FastAttn(const AttnParams& p_, const char* tab_, int head_)
-      : p(p_), tab(tab_), head(head_) {
-    tid = threadIdx.x;
+  __device__ Attn(const AttnParams& p_, char* smem_, int head_) : p(p_), smem(smem_), head(head_) {
+    const int tid = threadIdx.x;
     lane = tid & 63;
     wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     hh = lane >> 5;
     l32 = lane & 31;
-    sl2 = p.scale_log2;
-    rot_row = wave * 16 + (lane >> 2);
-    rot_q = lane & 3;
-    const int g0 = rot_q * PPL;
-    b0 = B::band(g0);
-    b1 = B::band(g0 + PPL - 1);
-    esplit = b0 == b1 ? PPL : B::start(b1) - g0;
-    c0 = (g0 - B::start(b0)) * 8;
-    c1 = (g0 - B::start(b1)) * 8;
-    // DMA unit i*64 + lane of this wave's 16 padded rows -> (row, 16-byte slot)
-    const uint32_t tok_bytes = (uint32_t)(p.n_heads * D * 2);
+    tok_bytes = (uint32_t)(p.n_heads * D * 2);
+    // DMA unit u = (wave * NDMA + i) * 64 + lane of a tile -> (row, 16-byte slot)
 #pragma unroll
-    for (int i = 0; i < DMA_PER_WAVE; ++i) {
-      const int u = i * 64 + lane;
-      const int rr = u / NU, c = u - rr * NU;
-      const int r = wave * 16 + rr;
-      const bool data = rr < 16 && c < NS;
+    for (int i = 0; i < NDMA; ++i) {
+      const int u = (wave * NDMA + i) * 64 + lane;
+      const int r = u / NU, c = u - r * NU;
+      const bool data = r < KT && c < NS;
       voff_k[i] = data ? (uint32_t)key_perm(r) * tok_bytes + c * 16 : kOutOfRange;
       voff_v[i] = data ? (uint32_t)r * tok_bytes + c * 16 : kOutOfRange;
     }
   }
 
+  __device__ char* kbuf(int st) const { return smem + st * TILE; }
+  __device__ char* vbuf(int st) const { return smem + (STAGES + st) * TILE; }
+
+  // Q' = bf16(rot(q) * log2(e)/sqrt(d)) as the QK^T B operand.
   __device__ void init_queries(int qt) {
+    const float sc = p.scale_log2;
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
       const int qrow = qt * QT + wave * 64 + qb * 32 + l32;
       const bool valid = qrow < p.n_q;
       int tq = 0, yq = 0, xq = 0;
-      if (valid) token_pos(p, qrow, p.q_t_index, tq, yq, xq);
+      if (valid) token_pos(p.g, qrow, p.q_t_index, tq, yq, xq);
       const uint16_t* qp = static_cast<const uint16_t*>(p.q) + ((size_t)qrow * p.n_heads + head) * D;
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
         const int off = 16 * c + 8 * hh;
         const uint4 w = valid ? *reinterpret_cast<const uint4*>(qp + off) : make_uint4(0, 0, 0, 0);
-        qreg[qb][c] = rotate_chunk_generic(p, w, off / 2, tq, yq, xq);
+        uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float2 cs = rope_cs(p.g, off / 2 + e, tq, yq, xq);
+          const float x0 = __uint_as_float(ws[e] << 16), x1 = __uint_as_float(ws[e] & 0xffff0000u);
+          ws[e] = pack_bf16((x0 * cs.x - x1 * cs.y) * sc, (x0 * cs.y + x1 * cs.x) * sc);
+        }
+        qreg[qb][c] = __builtin_bit_cast(bf16x8, make_uint4(ws[0], ws[1], ws[2], ws[3]));
       }
+    }
+    reset_accumulators();
+  }
+
+  __device__ void reset_accumulators() {
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
 #pragma unroll
       for (int i = 0; i < NDB; ++i) o[qb][i] = f32x16{};
       m_run[qb] = -INFINITY;
@@ -371,118 +190,74 @@ struct FastAttn {
     }
   }
 
-  // Queue the DMA of tile (s, n0) into LDS tiles kdst / vdst.  K row r holds
-  // key n0 + key_perm(r), V row r holds key n0 + r; rows past the segment's
-  // end repeat its last key (masked later, and always in bounds).  Wave w
-  // fills exactly rows 16w .. 16w+15, the rows it rotates later, so its own
-  // vmcnt wait covers every byte it reads back.
-  //
-  // The loads go through buffer resources whose range ends at the segment's
-  // last token: rows past it read as zero, and no address outside a segment
-  // is touched.  Per-lane byte offsets inside a tile are loop constants
-  // (voff_k / voff_v); lanes that land in LDS row padding get an offset past
-  // any range, so they write zeros there.
-  __device__ __forceinline__ void dma_tile(char* kdst, char* vdst, int s, int n0) {
-    const Segment& sg = p.seg[s];
-    const size_t tok_bytes = (size_t)sg.tok * 2;
-    const size_t off = (size_t)head * sg.head * 2 + (size_t)n0 * tok_bytes;
-    const int nrec = (int)((size_t)(sg.count - n0) * tok_bytes);
-    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<char*>(static_cast<const char*>(sg.k) + off), 0, nrec, kBufferConfig);
-    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<char*>(static_cast<const char*>(sg.v) + off), 0, nrec, kBufferConfig);
-    const int wbase = wave * 16 * RBP;
-#pragma unroll
-    for (int i = 0; i < DMA_PER_WAVE; ++i) {
-      if (i * 64 + 64 <= 16 * NU || i * 64 + lane < 16 * NU) {  // the wave's own 16 rows only
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (__attribute__((address_space(3))) void*)(kdst + wbase + i * 1024),
-                                                 16, voff_k[i], 0, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (__attribute__((address_space(3))) void*)(vdst + wbase + i * 1024),
-                                                 16, voff_v[i], 0, 0, 0);
-      }
-    }
+  // Buffer resources of tile (s, n0) of this head: the range ends at the
+  // segment's last token, so rows past it read as zero and nothing outside the
+  // segment is touched.  valid == false gives an empty range (all zeros).
+  __device__ __forceinline__ void rsrc(int s, int n0, bool valid, __amdgpu_buffer_rsrc_t& rk,
+                                       __amdgpu_buffer_rsrc_t& rv) const {
+    const Segment& sg = p.seg[valid ? s : 0];
+    const size_t off = valid ? (size_t)head * sg.head * 2 + (size_t)n0 * tok_bytes : 0;
+    const int nrec = valid ? (int)((size_t)(sg.count - n0) * tok_bytes) : 0;
+    rk = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(static_cast<const char*>(sg.k) + off),
+                                           0, nrec, kBufferConfig);
+    rv = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(static_cast<const char*>(sg.v) + off),
+                                           0, nrec, kBufferConfig);
   }
 
-  // Rotate, in place, the quarter-row of K this lane owns: for every pair,
-  // (x0, x1) -> (x0 c - x1 s, x0 s + x1 c) as two v_dot2 with packed-bf16
-  // (c, -s) and (s, c) from the LDS table.
-  __device__ __forceinline__ void rotate_tile(char* kt, int s, int n0) {
-    const Segment& sg = p.seg[s];
-    const int n = min(n0 + key_perm(rot_row), sg.count - 1);
-    int tt, y, x;
-    token_pos(p, n, sg.t_index, tt, y, x);
-    const int rt = tt * (B::NPT * 8);
-    const int rh = p.rope_h_off * 8 + y * (B::NPH * 8);
-    const int rw = p.rope_w_off * 8 + x * (B::NPW * 8);
-    const int r0 = (b0 == 0 ? rt : (b0 == 1 ? rh : rw)) + c0;
-    const int r1 = (b1 == 0 ? rt : (b1 == 1 ? rh : rw)) + c1;
-    char* base = kt + rot_row * RBP + rot_q * SPL * 16;
+  // This wave's share (NDMA instructions) of a K or V tile into LDS.
+  __device__ __forceinline__ void dma_k(char* dst, __amdgpu_buffer_rsrc_t r) const {
+    const uint32_t base = lds_addr(dst) + wave * NDMA * 1024;
 #pragma unroll
-    for (int i = 0; i < SPL; ++i) {
-      const uint4 w = *reinterpret_cast<const uint4*>(base + 16 * i);
-      const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
-      uint32_t out[4];
+    for (int i = 0; i < NDMA; ++i) dma16(r, base + i * 1024, voff_k[i]);
+  }
+  __device__ __forceinline__ void dma_v(char* dst, __amdgpu_buffer_rsrc_t r) const {
+    const uint32_t base = lds_addr(dst) + wave * NDMA * 1024;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int pe = 4 * i + e;
-        const uint2 cs = *reinterpret_cast<const uint2*>(tab + (pe < esplit ? r0 : r1) + 8 * pe);
-        const bf16x2 xv = __builtin_bit_cast(bf16x2, ws[e]);
-        const float y0 = __builtin_amdgcn_fdot2_f32_bf16(xv, __builtin_bit_cast(bf16x2, cs.x), 0.f, false);
-        const float y1 = __builtin_amdgcn_fdot2_f32_bf16(xv, __builtin_bit_cast(bf16x2, cs.y), 0.f, false);
-        out[e] = pack_bf16(y0, y1);
-      }
-      *reinterpret_cast<uint4*>(base + 16 * i) = make_uint4(out[0], out[1], out[2], out[3]);
-    }
+    for (int i = 0; i < NDMA; ++i) dma16(r, base + i * 1024, voff_v[i]);
   }
 
-  // S^T = K_rot Q_rot^T: [2 query blocks] x [2 key blocks] of 32x32
-  __device__ __forceinline__ void qk(const char* kt, f32x16 (&sc)[2][2]) {
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) { sc[qb][0] = f32x16{}; sc[qb][1] = f32x16{}; }
+  // S'^T of key block kb (32 keys) for both query blocks; the accumulators
+  // start from c0[qb].
+  __device__ __forceinline__ void qk_half(const char* kt, int kb, const f32x16 (&c0)[2],
+                                          f32x16 (&sc)[2]) const {
+    const char* kr = kt + (kb * 32 + l32) * RBP + hh * 16;
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
-      const char* kr = kt + l32 * RBP + hh * 16 + c * 32;
-      const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(kr);
-      const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(kr + 32 * RBP);
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(kr + c * 32);
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        sc[qb][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qreg[qb][c], sc[qb][0], 0, 0, 0);
-        sc[qb][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qreg[qb][c], sc[qb][1], 0, 0, 0);
-      }
+      for (int qb = 0; qb < 2; ++qb)
+        sc[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[qb][c], c == 0 ? c0[qb] : sc[qb], 0, 0, 0);
     }
   }
 
-  // Probabilities p = 2^(s*scale - m_run*scale) of query block qb packed to
-  // bf16 (the PV B operand); returns this lane's partial sum of the packed
+  // p = 2^s for the 16 scores of one (query block, key block), packed to bf16
+  // as the PV B operands of k-steps 2kb and 2kb+1 (register r holds key
+  // 16*(r/8) + 8hh + r%8 of the block); returns the lane's sum of the packed
   // values, so the normaliser sums the same rounded weights the PV uses.
-  __device__ __forceinline__ float probs(const f32x16 (&sq)[2], int qb, bf16x8 (&pq)[4]) {
-    const float mb = m_run[qb] * sl2;
+  __device__ __forceinline__ float soft(const f32x16& s, bf16x8& p_lo, bf16x8& p_hi) const {
+    uint32_t pw[8];
     float acc = 0.f;
 #pragma unroll
-    for (int kc = 0; kc < 4; ++kc) {
-      uint32_t pw[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sq[kc >> 1][(kc & 1) * 8 + 2 * e], sl2, -mb));
-        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sq[kc >> 1][(kc & 1) * 8 + 2 * e + 1], sl2, -mb));
-        pw[e] = pack_bf16(p0, p1);
-        acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw[e]), kOnes, acc, false);
-      }
-      pq[kc] = __builtin_bit_cast(bf16x8, make_uint4(pw[0], pw[1], pw[2], pw[3]));
+    for (int e = 0; e < 8; ++e) {
+      pw[e] = pack_bf16(__builtin_amdgcn_exp2f(s[2 * e]), __builtin_amdgcn_exp2f(s[2 * e + 1]));
+      acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw[e]), kOnes, acc, false);
     }
+    p_lo = __builtin_bit_cast(bf16x8, make_uint4(pw[0], pw[1], pw[2], pw[3]));
+    p_hi = __builtin_bit_cast(bf16x8, make_uint4(pw[4], pw[5], pw[6], pw[7]));
     return acc;
   }
 
-  // O^T += V^T P^T.  Lane (dv = 32db + l32, hh) needs keys 16kc + 8hh + j, j = 0..7:
-  // two transpose reads; in each, lane 4e + q of a 16-lane group points at
-  // row 16kc + 8hh + 4rd + e, dims 32db + 16*(group&1) + 4q .. +3.
-  __device__ __forceinline__ void pv(const char* vt, const bf16x8 (&pb)[2][4]) {
+  // O^T += V^T P^T over keys 32kb .. 32kb+31.  Lane (dv = 32db + l32, hh) needs
+  // keys 16kc + 8hh + j, j = 0..7: two transpose reads; in each, lane 4e + q of
+  // a 16-lane group points at row 16kc + 8hh + 4rd + e, dims
+  // 32db + 16*(group&1) + 4q .. +3.
+  __device__ __forceinline__ void pv_half(const char* vt, int kb, const bf16x8 (&pb)[2][4]) {
     const int grp = lane >> 4, i16 = lane & 15;
     const char* vl = vt + (8 * hh + (i16 >> 2)) * RBP + (16 * (grp & 1) + 4 * (i16 & 3)) * 2;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
-      for (int kc = 0; kc < 4; ++kc) {
+      for (int kc = 2 * kb; kc < 2 * kb + 2; ++kc) {
         i16x4 h[2];
 #pragma unroll
         for (int rd = 0; rd < 2; ++rd)
@@ -495,62 +270,48 @@ struct FastAttn {
       }
   }
 
-  // Full tile against the fixed running max, branch-free.  Returns true (for
-  // the whole wave) when some probability reached SUM_LIMIT or is not finite;
-  // the workgroup then recomputes everything with step_exact.
-  __device__ __forceinline__ bool step_fast(const char* kt, const char* vt) {
-    f32x16 sc[2][2];
-    qk(kt, sc);
-    bf16x8 pb[2][4];
-    const float r0 = probs(sc[0], 0, pb[0]);
-    const float r1 = probs(sc[1], 1, pb[1]);
-    l_run[0] += r0;
-    l_run[1] += r1;
-    pv(vt, pb);
-    return __any(!(r0 <= SUM_LIMIT) | !(r1 <= SUM_LIMIT));
-  }
-
   // Any tile, exact online softmax: keys past `count` are masked, the running
   // max follows the tile max and O and the normaliser are rescaled.
-  __device__ __forceinline__ void step_exact(const char* kt, const char* vt, int n0, int count) {
-    f32x16 sc[2][2];
-    qk(kt, sc);
-    // register r of key block kb holds key kb*32 + (r/8)*16 + hh*8 + r%8
+  __device__ void step_exact(const char* kt, const char* vt, int n0, int count) {
+    const f32x16 zero[2] = {f32x16{}, f32x16{}};
+    f32x16 sc[2][2];  // [key block][query block]
+    qk_half(kt, 0, zero, sc[0]);
+    qk_half(kt, 1, zero, sc[1]);
+    // register r of key block kb holds key kb*32 + 16*(r/8) + 8hh + r%8
     const int lim = count - n0 - hh * 8;
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-          if (kb * 32 + (r >> 3) * 16 + (r & 7) >= lim) sc[qb][kb][r] = -INFINITY;
+          if (kb * 32 + (r >> 3) * 16 + (r & 7) >= lim) sc[kb][qb][r] = -INFINITY;
     bf16x8 pb[2][4];
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
-      float m = sc[qb][0][0];
+      float m = sc[0][qb][0];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) m = fmaxf(m, sc[qb][kb][r]);
+        for (int r = 0; r < 16; ++r) m = fmaxf(m, sc[kb][qb][r]);
       m = fmaxf(m, __shfl_xor(m, 32, 64));
       const float m_new = fmaxf(m_run[qb], m);  // finite: every tile has a valid key
-      const float alpha = __builtin_amdgcn_exp2f((m_run[qb] - m_new) * sl2);
+      const float alpha = __builtin_amdgcn_exp2f(m_run[qb] - m_new);
       m_run[qb] = m_new;
 #pragma unroll
       for (int db = 0; db < NDB; ++db) o[qb][db] *= alpha;
-      l_run[qb] = l_run[qb] * alpha + probs(sc[qb], qb, pb[qb]);
-    }
-    pv(vt, pb);
-  }
-
-  __device__ void reset_accumulators() {
+      float rs = 0.f;
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
+      for (int kb = 0; kb < 2; ++kb) {
+        f32x16 t = sc[kb][qb];
 #pragma unroll
-      for (int i = 0; i < NDB; ++i) o[qb][i] = f32x16{};
-      m_run[qb] = -INFINITY;
-      l_run[qb] = 0.f;
+        for (int r = 0; r < 16; ++r) t[r] -= m_new;
+        rs += soft(t, pb[qb][2 * kb], pb[qb][2 * kb + 1]);
+      }
+      l_run[qb] = l_run[qb] * alpha + rs;
     }
+    pv_half(vt, 0, pb);
+    pv_half(vt, 1, pb);
   }
 
   __device__ void epilogue(int qt) {
@@ -575,102 +336,138 @@ struct FastAttn {
   }
 };
 
-__device__ __forceinline__ void wait_dma() { __builtin_amdgcn_s_waitcnt(0x3f70); }  // vmcnt(0)
-
-// Next full 64-key tile after (s, n0); returns false past the last one.
-__device__ inline bool next_full(const AttnParams& p, int& s, int& n0) {
-  n0 += kKeyTile;
-  if (n0 + kKeyTile > p.seg[s].count) {
-    ++s;
-    n0 = 0;
-    while (s < p.n_seg && p.seg[s].count < kKeyTile) ++s;
-  }
-  return s < p.n_seg;
-}
-
-template <int D, int DT, int DH>
+template <int D>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void attn_bf16_fast(const AttnParams p) {
-  using F = FastAttn<D, DT, DH>;
-  // Two K and two V tiles as distinct objects: the compiler can then tell the
-  // DMA into one buffer from the reads of the other and does not wait on it.
-  __shared__ __align__(16) char k0[F::TILE];
-  __shared__ __align__(16) char k1[F::TILE];
-  __shared__ __align__(16) char v0[F::TILE];
-  __shared__ __align__(16) char v1[F::TILE];
-  extern __shared__ __align__(16) char rope_lds[];
+void attn_bf16_kernel(const AttnParams p) {
+  using A = Attn<D>;
+  __shared__ __align__(16) char smem[2 * A::STAGES * A::TILE];
+  __shared__ int bad_flag[4];
 
   int head, qt;
   if (!map_workgroup(p, head, qt)) return;
+  A a(p, smem, head);
 
-  // packed-bf16 rotation table -> LDS (read by the key rotation of every tile)
-  {
-    const int n16 = (p.rope_bytes + 15) >> 4;
-    const uint4* src = reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(p.rope) + p.rope_bytes);
-    for (int i = threadIdx.x; i < n16; i += 256) reinterpret_cast<uint4*>(rope_lds)[i] = src[i];
-  }
-  F a(p, rope_lds, head);
-  // Full 64-key tiles go through the pipelined fast loop; the ragged last tile
-  // of each segment (and, after an overflow, everything) through exact steps.
-  // Tile order does not change the softmax result.
-  __shared__ int ovf[2][4];  // per-wave overflow flags, one set per unrolled half
-  int s = 0;
-  while (s < p.n_seg && p.seg[s].count < F::KT) ++s;
-  const bool have_full = s < p.n_seg;
-  if (have_full) a.dma_tile(k0, v0, s, 0);
-  a.init_queries(qt);
-  wait_dma();
-  __syncthreads();  // the table and the first tile are in LDS
-  bool overflow = false;
-  if (have_full) {
-    a.rotate_tile(k0, s, 0);
+  int n_full = 0;
+  for (int s = 0; s < p.n_seg; ++s) n_full += p.seg[s].count / A::KT;
+
+  bool bad = false;
+  if (n_full > 0) {
+    // K and V of tile t go to stage t % 3.  DMA groups: K0 alone, then
+    // {K1, V0}, {K2, V1}, and iteration j issues {K(j+3), V(j+2)}, so at the
+    // top of iteration j a wave waits for all but its newest group.  Tiles past
+    // the last one load as zeros into stages nobody reads.
+    TileCursor ck, cv;  // next K tile to load, next V tile to load
+    ck.first(p);
+    cv = ck;
+    int kt_next = 0, vt_next = 0;
+    auto load_k = [&]() {
+      __amdgpu_buffer_rsrc_t rk, rv;
+      a.rsrc(ck.s, ck.n0, kt_next < n_full, rk, rv);
+      a.dma_k(a.kbuf(kt_next % A::STAGES), rk);
+      ++kt_next;
+      ck.next(p);
+    };
+    auto load_v = [&]() {
+      __amdgpu_buffer_rsrc_t rk, rv;
+      a.rsrc(cv.s, cv.n0, vt_next < n_full, rk, rv);
+      a.dma_v(a.vbuf(vt_next % A::STAGES), rv);
+      ++vt_next;
+      cv.next(p);
+    };
+    load_k();  // K0
+    a.init_queries(qt);
+    load_k();  // K1
+    load_v();  // V0
+    load_k();  // K2
+    load_v();  // V1
+    wait_vm<4 * A::NDMA>();  // K0 landed
     __syncthreads();
-    int s1 = s, n1 = 0;
-    bool more = next_full(p, s1, n1);
-    if (more) a.dma_tile(k1, v1, s1, n1);
-    a.step_exact(k0, v0, 0, p.seg[s].count);  // sets the running max
-    if (more) {
-      wait_dma();
-      a.rotate_tile(k1, s1, n1);
-      __syncthreads();
-      more = next_full(p, s1, n1);
-      while (true) {
-        if (more) a.dma_tile(k0, v0, s1, n1);
-        ovf[0][a.wave] = a.step_fast(k1, v1);
-        if (more) {
-          wait_dma();
-          a.rotate_tile(k0, s1, n1);
-        }
-        __syncthreads();
-        if (ovf[0][0] | ovf[0][1] | ovf[0][2] | ovf[0][3]) { overflow = true; break; }
-        if (!more) break;
-        more = next_full(p, s1, n1);
 
-        if (more) a.dma_tile(k1, v1, s1, n1);
-        ovf[1][a.wave] = a.step_fast(k0, v0);
-        if (more) {
-          wait_dma();
-          a.rotate_tile(k1, s1, n1);
-        }
-        __syncthreads();
-        if (ovf[1][0] | ovf[1][1] | ovf[1][2] | ovf[1][3]) { overflow = true; break; }
-        if (!more) break;
-        more = next_full(p, s1, n1);
+    // First tile, exact: sets each row's reference max m.
+    const f32x16 zero[2] = {f32x16{}, f32x16{}};
+    f32x16 s_lo[2], s_hi[2];  // [query block]: keys 0..31 / keys 32..63 of the tile
+    a.qk_half(a.kbuf(0), 0, zero, s_lo);
+    a.qk_half(a.kbuf(0), 1, zero, s_hi);
+    f32x16 cm[2];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      float m = s_lo[qb][0];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) m = fmaxf(fmaxf(m, s_lo[qb][r]), s_hi[qb][r]);
+      m = fmaxf(m, __shfl_xor(m, 32, 64));
+      a.m_run[qb] = m;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        cm[qb][r] = -m;
+        s_lo[qb][r] -= m;
+        s_hi[qb][r] -= m;
       }
     }
+    bf16x8 pb[2][4];
+    float l0 = a.soft(s_lo[0], pb[0][0], pb[0][1]);
+    float l1 = a.soft(s_lo[1], pb[1][0], pb[1][1]);
+
+    // Steady state: iteration j = QK^T of tile j+1 and PV of tile j.
+    // Entering it, pb[.][0..1] (keys 0..31 of tile j) and s_hi (keys 32..63
+    // of tile j, already shifted by -m) are ready.
+    for (int j = 0; j + 1 < n_full; ++j) {
+      wait_vm<2 * A::NDMA>();  // K(j+1) and V(j) landed (own share)
+      __syncthreads();         // ... everyone's share; stages of K(j), V(j-1) free
+      load_k();                // K(j+3)
+      load_v();                // V(j+2)
+      const char* kt = a.kbuf((j + 1) % A::STAGES);
+      const char* vt = a.vbuf(j % A::STAGES);
+      f32x16 n_lo[2], n_hi[2];
+      a.qk_half(kt, 0, cm, n_lo);
+      l0 += a.soft(s_hi[0], pb[0][2], pb[0][3]);
+      a.pv_half(vt, 0, pb);
+      l1 += a.soft(s_hi[1], pb[1][2], pb[1][3]);
+      a.qk_half(kt, 1, cm, n_hi);
+      bf16x8 nb[2][2];
+      l0 += a.soft(n_lo[0], nb[0][0], nb[0][1]);
+      a.pv_half(vt, 1, pb);
+      l1 += a.soft(n_lo[1], nb[1][0], nb[1][1]);
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        s_hi[qb] = n_hi[qb];
+        pb[qb][0] = nb[qb][0];
+        pb[qb][1] = nb[qb][1];
+      }
+    }
+    // Drain: PV of the last full tile.
+    wait_vm<2 * A::NDMA>();
     __syncthreads();
+    {
+      const char* vt = a.vbuf((n_full - 1) % A::STAGES);
+      l0 += a.soft(s_hi[0], pb[0][2], pb[0][3]);
+      l1 += a.soft(s_hi[1], pb[1][2], pb[1][3]);
+      a.pv_half(vt, 0, pb);
+      a.pv_half(vt, 1, pb);
+    }
+    a.l_run[0] = l0;
+    a.l_run[1] = l1;
+    const bool mine = __any(!(l0 <= A::SUM_LIMIT) | !(l1 <= A::SUM_LIMIT));
+    if (a.lane == 0) bad_flag[a.wave] = mine;
+    wait_vm<0>();
+    __syncthreads();  // every DMA done, flags visible, stages free
+    bad = bad_flag[0] | bad_flag[1] | bad_flag[2] | bad_flag[3];
+  } else {
+    a.init_queries(qt);
   }
+
   // Exact, single-buffered passes: the ragged tiles, or every tile again after
-  // an overflow (rare: a score more than 14 powers of two above the first tile's max).
-  if (overflow) a.reset_accumulators();
-  for (int ss = 0; ss < p.n_seg; ++ss) {
-    const int cnt = p.seg[ss].count;
-    for (int nn = overflow ? 0 : cnt - cnt % F::KT; nn < cnt; nn += F::KT) {
-      a.dma_tile(k0, v0, ss, nn);
-      wait_dma();
-      a.rotate_tile(k0, ss, nn);
+  // an overflow.
+  if (bad) a.reset_accumulators();
+  for (int s = 0; s < p.n_seg; ++s) {
+    const int cnt = p.seg[s].count;
+    for (int n0 = bad ? 0 : cnt - cnt % A::KT; n0 < cnt; n0 += A::KT) {
+      __amdgpu_buffer_rsrc_t rk, rv;
+      a.rsrc(s, n0, true, rk, rv);
+      a.dma_k(a.kbuf(0), rk);
+      a.dma_v(a.vbuf(0), rv);
+      wait_vm<0>();
       __syncthreads();
-      a.step_exact(k0, v0, nn, cnt);
+      a.step_exact(a.kbuf(0), a.vbuf(0), n0, cnt);
       __syncthreads();
     }
   }
@@ -678,7 +475,7 @@ void attn_bf16_fast(const AttnParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// fp32: one query row per lane, 64-key tiles staged (rotated) in LDS.
+// fp32: one query row per lane, 64-key tiles staged in LDS.
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(64) void attn_f32_kernel(const AttnParams p) {
@@ -694,13 +491,13 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(const AttnParams p) {
   float q[D];
   {
     int tq = 0, yq = 0, xq = 0;
-    if (qvalid) token_pos(p, qrow, p.q_t_index, tq, yq, xq);
+    if (qvalid) token_pos(p.g, qrow, p.q_t_index, tq, yq, xq);
     const float* qp = static_cast<const float*>(p.q) + ((size_t)qrow * H + head) * D;
 #pragma unroll
     for (int i = 0; i < D / 2; ++i) {
       float x0 = 0.f, x1 = 0.f;
       if (qvalid) { x0 = qp[2 * i]; x1 = qp[2 * i + 1]; }
-      const float2 cs = pair_cs(p, pair_tab(p, i), tq, yq, xq);
+      const float2 cs = rope_cs(p.g, i, tq, yq, xq);
       q[2 * i] = x0 * cs.x - x1 * cs.y;
       q[2 * i + 1] = x0 * cs.y + x1 * cs.x;
     }
@@ -716,25 +513,10 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(const AttnParams p) {
     const float* kbase = static_cast<const float*>(sg.k) + (size_t)head * sg.head;
     const float* vbase = static_cast<const float*>(sg.v) + (size_t)head * sg.head;
     for (int n0 = 0; n0 < count; n0 += KT) {
-      for (int id = lane; id < KT * (D / 2); id += KT) {
-        const int r = id / (D / 2), pr = id % (D / 2);
-        const int n = n0 + r;
-        float y0 = 0.f, y1 = 0.f;
-        if (n < count) {
-          const float x0 = kbase[(size_t)n * sg.tok + 2 * pr];
-          const float x1 = kbase[(size_t)n * sg.tok + 2 * pr + 1];
-          int tt, y, x;
-          token_pos(p, n, sg.t_index, tt, y, x);
-          const float2 cs = pair_cs(p, pair_tab(p, pr), tt, y, x);
-          y0 = x0 * cs.x - x1 * cs.y;
-          y1 = x0 * cs.y + x1 * cs.x;
-        }
-        Ks[r][2 * pr] = y0;
-        Ks[r][2 * pr + 1] = y1;
-      }
       for (int id = lane; id < KT * D; id += KT) {
         const int r = id / D, dv = id % D;
         const int n = n0 + r;
+        Ks[r][dv] = n < count ? kbase[(size_t)n * sg.tok + dv] : 0.f;
         Vs[r][dv] = n < count ? vbase[(size_t)n * sg.tok + dv] : 0.f;
       }
       __syncthreads();
@@ -767,32 +549,13 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(const AttnParams p) {
 
 hipError_t launch_attention(const AttnParams& p_in, int dtype, int head_dim, hipStream_t s) {
   AttnParams p = p_in;
-  const int heads_per_xcd = (p.n_heads + 7) / 8;
   if (dtype == 0) {  // bf16
-    // the fast kernel's buffer ranges are 31-bit byte counts
-    size_t max_seg_bytes = 0;
-    for (int i = 0; i < p.n_seg; ++i) {
-      const size_t b = (size_t)p.seg[i].count * p.seg[i].tok * 2;
-      if (b > max_seg_bytes) max_seg_bytes = b;
-    }
-    const bool wan = p.np_h == p.np_w && p.np_h == head_dim / 6 && p.rope_bytes <= kMaxRopeLdsBytes &&
-                     max_seg_bytes < (size_t)kOutOfRange;
-    if (wan && (head_dim == 128 || head_dim == 64)) {
-      p.n_qtiles = (p.n_q + 255) / 256;
-      const dim3 grid(8 * heads_per_xcd * p.n_qtiles);
-      const size_t lds = ((size_t)p.rope_bytes + 15) / 16 * 16;
-      if (head_dim == 128)
-        hipLaunchKernelGGL((attn_bf16_fast<128, 44, 42>), grid, dim3(256), lds, s, p);
-      else
-        hipLaunchKernelGGL((attn_bf16_fast<64, 24, 20>), grid, dim3(256), lds, s, p);
-    } else {
-      p.n_qtiles = (p.n_q + 127) / 128;
-      const dim3 grid(8 * heads_per_xcd * p.n_qtiles);
-      if (head_dim == 128)
-        hipLaunchKernelGGL(attn_bf16_generic<128>, grid, dim3(256), 0, s, p);
-      else
-        hipLaunchKernelGGL(attn_bf16_generic<64>, grid, dim3(256), 0, s, p);
-    }
+    p.n_qtiles = (p.n_q + 255) / 256;
+    const dim3 grid(8 * ((p.n_heads + 7) / 8) * p.n_qtiles);
+    if (head_dim == 128)
+      hipLaunchKernelGGL(attn_bf16_kernel<128>, grid, dim3(256), 0, s, p);
+    else
+      hipLaunchKernelGGL(attn_bf16_kernel<64>, grid, dim3(256), 0, s, p);
   } else {
     p.n_qtiles = (p.n_q + kKeyTile - 1) / kKeyTile;
     const dim3 grid(p.n_qtiles, p.n_heads);

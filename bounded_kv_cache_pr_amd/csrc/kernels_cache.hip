@@ -1,7 +1,9 @@
 // Cache-maintenance kernels of the PR-Sink path on gfx950:
 //   kv_write     raw K/V [T][H][d] -> slot layout [t_pad][H][d] (contiguous copy)
-//   slot_copy    whole block slot (all layers) -> another slot; source and
-//                destination come from device state, so no host round trip
+//   rope_follow  raw keys -> keys rotated at a segment's current positions
+//   slot_copy    the first bytes of a block slot (all layers) -> another slot;
+//                source and destination come from device state, so no host
+//                round trip
 //   retrieve     fingerprint l2-normalisation + argmax over the bank (fp64)
 //   bank_update  exhaustive diversity replacement (fp64)
 #include "prsink_internal.h"
@@ -29,18 +31,18 @@ __global__ __launch_bounds__(256) void kv_write_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// slot_copy: grid-stride 16-byte copy of one block slot (all layers) to
-// another.  Reads the (source, destination) pair from device state; a
+// slot_copy: grid-stride 16-byte copy of the first copy_bytes of one block
+// slot to another.  Reads the (source, destination) pair from device state; a
 // negative source means there is nothing to copy.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void slot_copy_kernel(uint8_t* __restrict__ base,
-                                                        size_t slot_bytes,
+                                                        size_t slot_bytes, size_t copy_bytes,
                                                         const DevState* __restrict__ st) {
   const int src = st->copy_src, dst = st->copy_dst;
   if (src < 0 || src == dst) return;
   const uint4* __restrict__ s = reinterpret_cast<const uint4*>(base + (size_t)src * slot_bytes);
   uint4* __restrict__ d = reinterpret_cast<uint4*>(base + (size_t)dst * slot_bytes);
-  const size_t n = slot_bytes / 16;
+  const size_t n = copy_bytes / 16;
   const size_t stride = (size_t)gridDim.x * blockDim.x;
   size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   for (; i + 3 * stride < n; i += 4 * stride) {
@@ -48,6 +50,75 @@ __global__ __launch_bounds__(256) void slot_copy_kernel(uint8_t* __restrict__ ba
     d[i] = a; d[i + stride] = b; d[i + 2 * stride] = c; d[i + 3 * stride] = e;
   }
   for (; i < n; i += stride) d[i] = s[i];
+}
+
+// ---------------------------------------------------------------------------
+// rope_follow: RoPE follow for cached keys.  The cache keeps every key raw;
+// when a block takes a place in the cache layout (Ref at set-up, Static once,
+// each window block whenever the window slides, a bank entry at the Dynamic
+// Sink's place) its raw keys are rotated at the positions of that place, and
+// the current block's keys at the current positions on every call (review on
+// paper.rainbus.top, full-pipeline paragraph: raw keys re-rotated at their
+// current cache positions; novelty paragraph: position-consistent reuse).
+// Pair (x0, x1) of a band at angle a becomes (x0 cos a - x1 sin a,
+// x0 sin a + x1 cos a), in fp32, rounded once to the cache dtype.
+// Thread = one 16-byte chunk (4 bf16 pairs or 2 fp32 pairs) of one token and
+// head; grid = (chunks, layer, job).
+// ---------------------------------------------------------------------------
+__device__ inline float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ inline float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ inline uint32_t pack_bf16(float lo, float hi) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  bf16x2 v = {(__bf16)lo, (__bf16)hi};  // round to nearest even
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+__global__ __launch_bounds__(256) void rope_follow_kernel(const RotParams p) {
+  const RotJob& jb = p.job[blockIdx.z];
+  const size_t lay = (size_t)blockIdx.y * p.layer_bytes;
+  const char* __restrict__ src = jb.src + lay;
+  char* __restrict__ dst;
+  if (jb.from_state) {
+    const int cs = p.st->copy_src, cd = p.st->copy_dst;
+    if (cs < 0) return;
+    dst = p.block_base + (size_t)cd * p.slot_bytes + jb.dst_off + lay;
+  } else {
+    dst = jb.dst + lay;
+  }
+  const uint32_t per_head = (uint32_t)(p.head_dim * p.elem / 16);  // chunks per head row
+  const uint32_t per_tok = per_head * (uint32_t)p.n_heads;
+  const uint32_t total = per_tok * (uint32_t)p.n_tok;
+  const uint32_t stride = gridDim.x * 256;
+  for (uint32_t i = blockIdx.x * 256 + threadIdx.x; i < total; i += stride) {
+    const uint32_t n = i / per_tok;
+    const uint32_t c = (i - n * per_tok) % per_head;
+    int tt, y, x;
+    token_pos(p.g, (int)n, jb.t_index, tt, y, x);
+    uint4 w = reinterpret_cast<const uint4*>(src)[i];
+    if (p.elem == 2) {
+      uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float2 cs = rope_cs(p.g, (int)c * 4 + e, tt, y, x);
+        const float x0 = bf16_lo(ws[e]), x1 = bf16_hi(ws[e]);
+        ws[e] = pack_bf16(x0 * cs.x - x1 * cs.y, x0 * cs.y + x1 * cs.x);
+      }
+      w = make_uint4(ws[0], ws[1], ws[2], ws[3]);
+    } else {
+      float f[4] = {__uint_as_float(w.x), __uint_as_float(w.y), __uint_as_float(w.z),
+                    __uint_as_float(w.w)};
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const float2 cs = rope_cs(p.g, (int)c * 2 + e, tt, y, x);
+        const float x0 = f[2 * e], x1 = f[2 * e + 1];
+        f[2 * e] = x0 * cs.x - x1 * cs.y;
+        f[2 * e + 1] = x0 * cs.y + x1 * cs.x;
+      }
+      w = make_uint4(__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]),
+                     __float_as_uint(f[3]));
+    }
+    reinterpret_cast<uint4*>(dst)[i] = w;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -178,10 +249,8 @@ __global__ void state_init_kernel(DevState* st) {
 }  // namespace
 
 hipError_t launch_kv_write(const void* k_src, const void* v_src, void* k_dst0, void* v_dst0,
-                           void* k_dst1, void* v_dst1, int n_tok, int n_heads, int head_dim,
-                           int t_pad, int elem_bytes, hipStream_t s) {
-  (void)t_pad;
-  const size_t n_chunks = (size_t)n_tok * n_heads * head_dim * elem_bytes / 16;
+                           void* k_dst1, void* v_dst1, size_t bytes, hipStream_t s) {
+  const size_t n_chunks = bytes / 16;
   size_t blocks = (n_chunks + 255) / 256;
   if (blocks > 256 * 8) blocks = 256 * 8;
   hipLaunchKernelGGL(kv_write_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
@@ -191,13 +260,23 @@ hipError_t launch_kv_write(const void* k_src, const void* v_src, void* k_dst0, v
   return hipGetLastError();
 }
 
-hipError_t launch_slot_copy(char* block_base, size_t slot_bytes, const DevState* st,
-                            hipStream_t s) {
-  const size_t n16 = slot_bytes / 16;
+hipError_t launch_rope_follow(const RotParams& p, int n_layers, hipStream_t s) {
+  const size_t total = (size_t)p.n_tok * p.n_heads * p.head_dim * p.elem / 16;
+  size_t blocks = (total + 255) / 256;
+  const size_t cap = n_layers * p.n_jobs > 8 ? 512 : 4096;
+  if (blocks > cap) blocks = cap;
+  hipLaunchKernelGGL(rope_follow_kernel, dim3((unsigned)blocks, (unsigned)n_layers, (unsigned)p.n_jobs),
+                     dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_slot_copy(char* block_base, size_t slot_bytes, size_t copy_bytes,
+                            const DevState* st, hipStream_t s) {
+  const size_t n16 = copy_bytes / 16;
   size_t blocks = (n16 + 255) / 256;
   if (blocks > 256 * 16) blocks = 256 * 16;
   hipLaunchKernelGGL(slot_copy_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
-                     reinterpret_cast<uint8_t*>(block_base), slot_bytes, st);
+                     reinterpret_cast<uint8_t*>(block_base), slot_bytes, copy_bytes, st);
   return hipGetLastError();
 }
 

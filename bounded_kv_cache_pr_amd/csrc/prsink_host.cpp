@@ -63,15 +63,17 @@ bool magic_exact(uint32_t d, uint32_t n_max) {
 }
 
 // Arena layout (offsets in bytes from the arena base):
-//   [state | fingerprints | rope table] [Ref slot] [block slots...]
-// Block slots: Static, Dynamic, window 0..W-1, bank 0..M-1.  Each slot holds,
-// per layer, K [t_pad][H][d] then V [t_pad][H][d] (token-major, like the tensors the
-// caller passes, so every segment shares one row stride; rows past T stay zero).
+//   [state | fingerprints | rope table | current block's rotated K] [Ref slot] [block slots...]
+// Block slots: Static, Dynamic, window 0..W-1, bank 0..M-1.  A slot holds three
+// regions of n_layers tensors each, every tensor [t_pad][H][d] (token-major,
+// like the tensors the caller passes, so every segment shares one row stride;
+// rows past T stay zero): raw K, V, and K rotated at the positions of the
+// slot's current place in the layout (a bank entry: the Dynamic Sink's place).
 struct Layout {
   int elem, tpf, tb, tr, tb_pad, tr_pad;
-  size_t kv_b, layer_b, slot_b;   // block slot: one tensor, one layer, whole slot
-  size_t kv_r, layer_r, slot_r;   // Ref slot
-  size_t off_state, off_phi_bank, off_phi_cur, off_rope, off_ref, off_blocks, total;
+  size_t kv_b, slot_b;   // block slot: one tensor of one layer, whole slot
+  size_t kv_r, slot_r;   // Ref slot
+  size_t off_state, off_phi_bank, off_phi_cur, off_rope, off_cur_rot, off_ref, off_blocks, total;
   int n_t, np_t, np_h, np_w, rope_h_off, rope_w_off, rope_entries;
   int n_block_slots;
 };
@@ -101,6 +103,11 @@ bool check_config(const pr_sink_config* c) {
   const uint32_t n_max = (uint32_t)(tpf * (c->block_frames > c->ref_frames ? c->block_frames : c->ref_frames));
   if (!magic_exact((uint32_t)tpf, n_max) || !magic_exact((uint32_t)c->lat_w, (uint32_t)tpf))
     return fail(PR_SINK_EINVAL, "latent frame %dx%d too large for 32-bit position division", c->lat_h, c->lat_w), false;
+  // rotation kernels index 16-byte chunks of one block's keys with 32-bit ints;
+  // attention buffer ranges (one segment of one layer) stay below 2^31 bytes
+  const long long elem = c->dtype == PR_SINK_BF16 ? 2 : 4;
+  const long long seg_bytes = (long long)n_max * c->n_heads * c->head_dim * elem;
+  if (seg_bytes >= (1ll << 31)) return fail(PR_SINK_EINVAL, "one block of one layer must stay below 2 GiB"), false;
   return true;
 }
 
@@ -113,12 +120,10 @@ Layout make_layout(const pr_sink_config* c) {
   L.tb_pad = pad_tokens(L.tb);
   L.tr_pad = pad_tokens(L.tr);
   const size_t hd = (size_t)c->n_heads * c->head_dim * L.elem;
-  L.kv_b = hd * L.tb_pad;
-  L.layer_b = 2 * L.kv_b;
-  L.slot_b = align_up(L.layer_b * c->n_layers, kAlign);
-  L.kv_r = hd * L.tr_pad;
-  L.layer_r = 2 * L.kv_r;
-  L.slot_r = align_up(L.layer_r * c->n_layers, kAlign);
+  L.kv_b = align_up(hd * L.tb_pad, 256);
+  L.slot_b = align_up(3 * L.kv_b * c->n_layers, kAlign);
+  L.kv_r = align_up(hd * L.tr_pad, 256);
+  L.slot_r = align_up(3 * L.kv_r * c->n_layers, kAlign);
   L.n_block_slots = 2 + c->window_slots + c->bank_size;
   // temporal positions: Ref, Static, Dynamic, W-1 previous blocks, current
   L.n_t = c->ref_frames + (c->window_slots + 2) * c->block_frames;
@@ -135,8 +140,10 @@ Layout make_layout(const pr_sink_config* c) {
   off = align_up(off + sizeof(double) * c->bank_size * c->fp_dim, 256);
   L.off_phi_cur = off;
   off = align_up(off + sizeof(double) * c->fp_dim, 256);
-  L.off_rope = off;  // fp32 (cos, sin) table, then the packed-bf16 rotation table
-  off = align_up(off + 16 * (size_t)L.rope_entries, kAlign);
+  L.off_rope = off;  // fp32 (cos, sin) table
+  off = align_up(off + 8 * (size_t)L.rope_entries, kAlign);
+  L.off_cur_rot = off;
+  off = align_up(off + L.kv_b, kAlign);
   L.off_ref = off;
   off += L.slot_r;
   L.off_blocks = off;
@@ -145,20 +152,12 @@ Layout make_layout(const pr_sink_config* c) {
   return L;
 }
 
-// bf16 bits of a float, round to nearest even.
-uint32_t bf16_bits(float f) {
-  uint32_t u;
-  std::memcpy(&u, &f, 4);
-  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-}
-
-// cos/sin of every (band, position, pair), computed in double.  Two tables of
-// rope_entries 8-byte entries each: fp32 (cos, sin), then the same angles as
-// packed bf16 pairs (cos, -sin) and (sin, cos), the operands of the two
-// v_dot2 products that rotate one bf16 key pair.
+// cos/sin of every (band, position, pair), computed in double and stored as
+// fp32 (cos, sin): the t band over the n_t temporal rows, then h, then w.  The
+// angle of pair i of a band of D dims at position p is p * theta^(-2i/D).
 std::vector<uint32_t> rope_table(const pr_sink_config* c, const Layout& L) {
   const size_t E = (size_t)L.rope_entries;
-  std::vector<uint32_t> t(4 * E);
+  std::vector<uint32_t> t(2 * E);
   auto fill = [&](int base, int npos, int pos0, int band_dim) {
     const int np = band_dim / 2;
     for (int ps = 0; ps < npos; ++ps)
@@ -169,8 +168,6 @@ std::vector<uint32_t> rope_table(const pr_sink_config* c, const Layout& L) {
         const size_t e = (size_t)(base + ps * np + i);
         std::memcpy(&t[2 * e], &cs, 4);
         std::memcpy(&t[2 * e + 1], &sn, 4);
-        t[2 * E + 2 * e] = bf16_bits(cs) | (bf16_bits(-sn) << 16);
-        t[2 * E + 2 * e + 1] = bf16_bits(sn) | (bf16_bits(cs) << 16);
       }
   };
   fill(0, L.n_t, c->t0, c->rope_dims[0]);
@@ -193,6 +190,11 @@ struct pr_sink_cache {
   std::vector<uint8_t> ref_set, written;
 
   char* block_slot(int bs) const { return arena + lay.off_blocks + (size_t)bs * lay.slot_b; }
+  char* ref_slot() const { return arena + lay.off_ref; }
+  // raw K, V and rotated K of one layer inside a slot whose tensors are kv bytes
+  size_t k_off(int l, size_t kv) const { return (size_t)l * kv; }
+  size_t v_off(int l, size_t kv) const { return ((size_t)cfg.n_layers + l) * kv; }
+  size_t r_off(int l, size_t kv) const { return (2 * (size_t)cfg.n_layers + l) * kv; }
   DevState* state() const { return reinterpret_cast<DevState*>(arena + lay.off_state); }
   double* phi_bank() const { return reinterpret_cast<double*>(arena + lay.off_phi_bank); }
   double* phi_cur() const { return reinterpret_cast<double*>(arena + lay.off_phi_cur); }
@@ -235,6 +237,53 @@ void segment_table(const pr_sink_cache* c, int* tokens, int* t_index) {
     tokens[s] = id >= 0 ? c->lay.tb : 0; t_index[s++] = t; t += fb;
   }
   tokens[s] = c->lay.tb; t_index[s++] = t;                                 // current block
+}
+
+RopeGeom rope_geom(const pr_sink_cache* c) {
+  const Layout& L = c->lay;
+  RopeGeom g{};
+  g.rope = c->rope();
+  g.np_t = L.np_t;
+  g.np_h = L.np_h;
+  g.np_w = L.np_w;
+  g.rope_h_off = L.rope_h_off;
+  g.rope_w_off = L.rope_w_off;
+  g.lat_w = c->cfg.lat_w;
+  g.hw = L.tpf;
+  g.magic_hw = magic_for((uint32_t)L.tpf);
+  g.one_hw = L.tpf == 1;
+  g.magic_w = magic_for((uint32_t)c->cfg.lat_w);
+  g.one_w = c->cfg.lat_w == 1;
+  return g;
+}
+
+// Rotation launch over n_tok tokens per layer; consecutive layers of source
+// and destination lie layer_bytes apart.
+RotParams rot_params(const pr_sink_cache* c, int n_tok, size_t layer_bytes) {
+  RotParams r{};
+  r.g = rope_geom(c);
+  r.st = c->state();
+  r.block_base = c->block_slot(0);
+  r.slot_bytes = (int64_t)c->lay.slot_b;
+  r.layer_bytes = (int64_t)layer_bytes;
+  r.n_tok = n_tok;
+  r.n_heads = c->cfg.n_heads;
+  r.head_dim = c->cfg.head_dim;
+  r.elem = c->lay.elem;
+  return r;
+}
+
+void add_job(RotParams& r, const void* src, void* dst, int t_index) {
+  RotJob& j = r.job[r.n_jobs++];
+  j.src = static_cast<const char*>(src);
+  j.dst = static_cast<char*>(dst);
+  j.dst_off = 0;
+  j.t_index = t_index;
+  j.from_state = 0;
+}
+
+size_t block_bytes(const pr_sink_cache* c, int n_tok) {
+  return (size_t)n_tok * c->cfg.n_heads * c->cfg.head_dim * c->lay.elem;
 }
 
 }  // namespace
@@ -298,9 +347,14 @@ int pr_sink_set_ref(pr_sink_cache* c, int32_t layer, const void* k_raw, const vo
   if (c->open) return fail(PR_SINK_ESTATE, "set_ref while block %d is open", c->next_block);
   if (!c->dry) {
     const Layout& L = c->lay;
-    char* base = c->arena + L.off_ref + (size_t)layer * L.layer_r;
-    PRS_HIP(launch_kv_write(k_raw, v_raw, base, base + L.kv_r, nullptr, nullptr, L.tr,
-                            c->cfg.n_heads, c->cfg.head_dim, L.tr_pad, L.elem, as_stream(stream)));
+    hipStream_t s = as_stream(stream);
+    char* ref = c->ref_slot();
+    PRS_HIP(launch_kv_write(k_raw, v_raw, ref + c->k_off(layer, L.kv_r), ref + c->v_off(layer, L.kv_r),
+                            nullptr, nullptr, block_bytes(c, L.tr), s));
+    // the Ref Sink's place never moves: rotate its keys once
+    RotParams r = rot_params(c, L.tr, L.kv_r);
+    add_job(r, ref + c->k_off(layer, L.kv_r), ref + c->r_off(layer, L.kv_r), 0);
+    PRS_HIP(launch_rope_follow(r, 1, s));
   }
   c->ref_set[layer] = 1;
   return PR_SINK_OK;
@@ -320,10 +374,27 @@ int pr_sink_retrieve(pr_sink_cache* c, int32_t block, const float* fp_raw_dev,
   // several distinct blocks of which at most one is block-1.
   const bool candidate = c->bank_count >= 2 || (c->bank_count == 1 && block - 1 != 0);
   if (!c->dry) {
+    const pr_sink_config& g = c->cfg;
+    const Layout& L = c->lay;
     hipStream_t s = as_stream(stream);
-    PRS_HIP(launch_retrieve(fp_raw_dev, c->phi_cur(), c->phi_bank(), c->state(), c->cfg.fp_dim,
+    PRS_HIP(launch_retrieve(fp_raw_dev, c->phi_cur(), c->phi_bank(), c->state(), g.fp_dim,
                             c->bank_count, block, c->bs_dynamic(), c->bs_bank(0), slot_out_dev, s));
-    PRS_HIP(launch_slot_copy(c->block_slot(0), c->lay.slot_b, c->state(), s));
+    // Dynamic Sink <- bank entry r: raw K, V and K already rotated at the Dynamic place
+    PRS_HIP(launch_slot_copy(c->block_slot(0), L.slot_b, 3 * L.kv_b * g.n_layers, c->state(), s));
+    // RoPE follow for the blocks whose place changes as this block opens: every
+    // previous window block moves one place, and block 0 becomes the Static Sink.
+    RotParams r = rot_params(c, L.tb, L.kv_b);
+    for (int j = 0; j < g.window_slots - 1; ++j) {
+      const int id = block - (g.window_slots - 1) + j;
+      if (id < 0) continue;
+      char* w = c->block_slot(c->bs_window(id % g.window_slots));
+      add_job(r, w + c->k_off(0, L.kv_b), w + c->r_off(0, L.kv_b), g.ref_frames + (2 + j) * g.block_frames);
+    }
+    if (block == 1) {
+      char* st = c->block_slot(c->bs_static());
+      add_job(r, st + c->k_off(0, L.kv_b), st + c->r_off(0, L.kv_b), g.ref_frames);
+    }
+    if (r.n_jobs) PRS_HIP(launch_rope_follow(r, g.n_layers, s));
   }
   c->dyn_present = candidate;
   c->open = true;
@@ -346,28 +417,29 @@ int pr_sink_attend(pr_sink_cache* c, int32_t layer, const void* q_raw, const voi
   int tokens[kMaxSegments], t_index[kMaxSegments];
   segment_table(c, tokens, t_index);
   const int n_seg = g.window_slots + 3;
+  hipStream_t st = as_stream(stream);
+  // the current block's keys, rotated at the current positions
+  char* cur_rot = c->arena + L.off_cur_rot;
+  {
+    RotParams r = rot_params(c, L.tb, 0);
+    add_job(r, k_cur_raw, cur_rot, t_index[n_seg - 1]);
+    PRS_HIP(launch_rope_follow(r, 1, st));
+  }
   AttnParams p{};
   const int64_t D = g.head_dim;
-  auto cached = [&](Segment& sg, const char* slot_base, size_t layer_bytes, size_t kv_bytes, int t_pad) {
-    const char* kb = slot_base + (size_t)layer * layer_bytes;
-    sg.k = kb;
-    sg.v = kb + kv_bytes;
-    sg.tok = (int64_t)g.n_heads * D;
-    sg.head = D;
-    (void)t_pad;
-  };
   const int b = c->next_block;
   for (int s = 0; s < n_seg; ++s) {
     Segment& sg = p.seg[s];
     sg.count = tokens[s];
     sg.t_index = t_index[s];
+    sg.tok = (int64_t)g.n_heads * D;
+    sg.head = D;
     if (s == 0) {
-      cached(sg, c->arena + L.off_ref, L.layer_r, L.kv_r, L.tr_pad);
-    } else if (s == n_seg - 1) {  // current block, caller's [T][H][d]
-      sg.k = k_cur_raw;
+      sg.k = c->ref_slot() + c->r_off(layer, L.kv_r);
+      sg.v = c->ref_slot() + c->v_off(layer, L.kv_r);
+    } else if (s == n_seg - 1) {  // current block: rotated copy, caller's V
+      sg.k = cur_rot;
       sg.v = v_cur_raw;
-      sg.tok = (int64_t)g.n_heads * D;
-      sg.head = D;
     } else {
       int bs;
       if (s == 1) bs = c->bs_static();
@@ -376,30 +448,19 @@ int pr_sink_attend(pr_sink_cache* c, int32_t layer, const void* q_raw, const voi
         const int id = b - (g.window_slots - 1) + (s - 3);
         bs = c->bs_window(id >= 0 ? id % g.window_slots : 0);
       }
-      cached(sg, c->block_slot(bs), L.layer_b, L.kv_b, L.tb_pad);
+      sg.k = c->block_slot(bs) + c->r_off(layer, L.kv_b);
+      sg.v = c->block_slot(bs) + c->v_off(layer, L.kv_b);
     }
   }
   p.q = q_raw;
   p.out = out;
-  p.rope = c->rope();
+  p.g = rope_geom(c);
   p.n_seg = n_seg;
   p.n_q = L.tb;
   p.n_heads = g.n_heads;
-  p.lat_w = g.lat_w;
-  p.hw = L.tpf;
   p.q_t_index = t_index[n_seg - 1];
-  p.np_t = L.np_t;
-  p.np_h = L.np_h;
-  p.np_w = L.np_w;
-  p.rope_h_off = L.rope_h_off;
-  p.rope_w_off = L.rope_w_off;
-  p.rope_bytes = L.rope_entries * 8;
   p.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)g.head_dim));
-  p.magic_hw = magic_for((uint32_t)L.tpf);
-  p.one_hw = L.tpf == 1;
-  p.magic_w = magic_for((uint32_t)g.lat_w);
-  p.one_w = g.lat_w == 1;
-  PRS_HIP(launch_attention(p, g.dtype, g.head_dim, as_stream(stream)));
+  PRS_HIP(launch_attention(p, g.dtype, g.head_dim, st));
   return PR_SINK_OK;
 }
 
@@ -413,10 +474,12 @@ int pr_sink_clean_kv_write(pr_sink_cache* c, int32_t layer, const void* k_raw, c
   if (!c->dry) {
     const Layout& L = c->lay;
     const int b = c->next_block;
-    char* w = c->block_slot(c->bs_window(b % c->cfg.window_slots)) + (size_t)layer * L.layer_b;
-    char* st = b == 0 ? c->block_slot(c->bs_static()) + (size_t)layer * L.layer_b : nullptr;
-    PRS_HIP(launch_kv_write(k_raw, v_raw, w, w + L.kv_b, st, st ? st + L.kv_b : nullptr, L.tb,
-                            c->cfg.n_heads, c->cfg.head_dim, L.tb_pad, L.elem, as_stream(stream)));
+    char* w = c->block_slot(c->bs_window(b % c->cfg.window_slots));
+    char* st = b == 0 ? c->block_slot(c->bs_static()) : nullptr;
+    PRS_HIP(launch_kv_write(k_raw, v_raw, w + c->k_off(layer, L.kv_b), w + c->v_off(layer, L.kv_b),
+                            st ? st + c->k_off(layer, L.kv_b) : nullptr,
+                            st ? st + c->v_off(layer, L.kv_b) : nullptr, block_bytes(c, L.tb),
+                            as_stream(stream)));
   }
   c->written[layer] = 1;
   return PR_SINK_OK;
@@ -431,10 +494,18 @@ int pr_sink_bank_update(pr_sink_cache* c, int32_t block, void* stream) {
   if (block < g.bank_fill_blocks) {
     if (!c->dry) {
       hipStream_t s = as_stream(stream);
+      const Layout& L = c->lay;
+      const int ws = c->bs_window(block % g.window_slots);
       PRS_HIP(launch_bank_update(c->phi_cur(), c->phi_bank(), c->state(), g.fp_dim, g.bank_size,
-                                 c->bank_count, block, c->bs_window(block % g.window_slots),
-                                 c->bs_bank(0), s));
-      PRS_HIP(launch_slot_copy(c->block_slot(0), c->lay.slot_b, c->state(), s));
+                                 c->bank_count, block, ws, c->bs_bank(0), s));
+      // the written entry gets the block's raw K and V, and its K rotated at
+      // the Dynamic Sink's place, the only place a bank entry is attended from
+      PRS_HIP(launch_slot_copy(c->block_slot(0), L.slot_b, 2 * L.kv_b * g.n_layers, c->state(), s));
+      RotParams r = rot_params(c, L.tb, L.kv_b);
+      add_job(r, c->block_slot(ws) + c->k_off(0, L.kv_b), nullptr, g.ref_frames + g.block_frames);
+      r.job[0].from_state = 1;
+      r.job[0].dst_off = (int64_t)c->r_off(0, L.kv_b);
+      PRS_HIP(launch_rope_follow(r, g.n_layers, s));
     }
     if (c->bank_count < g.bank_size) ++c->bank_count;
   }
@@ -465,26 +536,27 @@ int pr_sink_bank_state(pr_sink_cache* c, int32_t* ids_host, double* fp_host, int
 }
 
 int pr_sink_slot_view(const pr_sink_cache* c, int32_t slot, int32_t layer, void** k_dev,
-                      void** v_dev, int32_t* t_pad_out) {
+                      void** v_dev, void** k_rot_dev, int32_t* t_pad_out) {
   if (int e = check_layer(c, layer)) return e;
   if (!k_dev || !v_dev || !t_pad_out) return fail(PR_SINK_EINVAL, "NULL output pointer");
   if (c->dry) return fail(PR_SINK_EINVAL, "dry-run cache has no arena");
   const Layout& L = c->lay;
   const int n_slots = 1 + L.n_block_slots;
   if (slot < 0 || slot >= n_slots) return fail(PR_SINK_EINVAL, "slot %d out of range", slot);
-  char* k;
+  char* base;
   size_t kv;
   if (slot == PR_SINK_SLOT_REF) {
-    k = c->arena + L.off_ref + (size_t)layer * L.layer_r;
+    base = c->ref_slot();
     kv = L.kv_r;
     *t_pad_out = L.tr_pad;
   } else {
-    k = c->block_slot(slot - 1) + (size_t)layer * L.layer_b;
+    base = c->block_slot(slot - 1);
     kv = L.kv_b;
     *t_pad_out = L.tb_pad;
   }
-  *k_dev = k;
-  *v_dev = k + kv;
+  *k_dev = base + c->k_off(layer, kv);
+  *v_dev = base + c->v_off(layer, kv);
+  if (k_rot_dev) *k_rot_dev = base + c->r_off(layer, kv);
   return PR_SINK_OK;
 }
 

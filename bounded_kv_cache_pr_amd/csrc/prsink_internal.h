@@ -11,13 +11,49 @@ namespace prsink {
 constexpr int kMaxSegments = 8;   // Ref, Static, Dynamic, <= 4 previous window blocks, current
 constexpr int kMaxBank = 8;
 constexpr int kKeyTile = 64;      // keys per attention tile; slot token counts pad to this
-constexpr int kMaxRopeLdsBytes = 48 * 1024;  // cos/sin table size the fast kernel stages in LDS
+constexpr int kMaxRotJobs = 6;    // rotation jobs per rope_follow launch
+
+// Geometry of the 3D RoPE tables and of the latent grid, shared by every
+// kernel that rotates.  The cos/sin table holds float2 (cos, sin) entries:
+// t band [n_t][np_t], then h band [lat_h][np_h] at rope_h_off, then w band
+// [lat_w][np_w] at rope_w_off.  Token n of a segment sits in frame n / hw, row
+// (n % hw) / lat_w, column n % lat_w; the divisions use multiply-high magic
+// numbers the host checked to be exact over the token ranges in use
+// (n / d == umulhi(n, magic) + n * one, and a divisor of 1 has magic 0, one 1).
+struct RopeGeom {
+  const float2* rope;
+  int32_t np_t, np_h, np_w;
+  int32_t rope_h_off, rope_w_off;
+  int32_t lat_w, hw;
+  uint32_t magic_hw, one_hw, magic_w, one_w;
+};
+
+__device__ inline uint32_t div_magic(uint32_t n, uint32_t magic, uint32_t one) {
+  return __umulhi(n, magic) + n * one;
+}
+
+// (temporal row, latent row, latent column) of token n of a segment whose
+// first frame uses temporal row t_index.
+__device__ inline void token_pos(const RopeGeom& g, int n, int t_index, int& tt, int& y, int& x) {
+  const int f = div_magic(n, g.magic_hw, g.one_hw), j = n - f * g.hw;
+  y = div_magic(j, g.magic_w, g.one_w);
+  x = j - y * g.lat_w;
+  tt = t_index + f;
+}
+
+// cos/sin of RoPE pair `pair` (adjacent elements 2*pair, 2*pair+1 of a head)
+// at position (tt, y, x): the t band covers the first np_t pairs, then h, then w.
+__device__ inline float2 rope_cs(const RopeGeom& g, int pair, int tt, int y, int x) {
+  if (pair < g.np_t) return g.rope[tt * g.np_t + pair];
+  if (pair < g.np_t + g.np_h) return g.rope[g.rope_h_off + y * g.np_h + pair - g.np_t];
+  return g.rope[g.rope_w_off + x * g.np_w + pair - g.np_t - g.np_h];
+}
 
 // One attended segment of the cache as the attention kernel sees it.  K and V
 // share one layout: element (token n, head h, dim i) is at n*tok + h*head + i.
 struct Segment {
-  const void* k;        // raw keys, head 0, token 0
-  const void* v;        // values, head 0, token 0
+  const void* k;        // keys already rotated at this segment's current positions
+  const void* v;        // values
   int64_t tok;          // elements between consecutive tokens of one head
   int64_t head;         // elements between heads
   int32_t count;        // tokens attended (0 = segment empty)
@@ -28,23 +64,13 @@ struct AttnParams {
   Segment seg[kMaxSegments];
   const void* q;        // [T][H][d] raw queries of the current block
   void* out;            // [T][H][d]
-  const float2* rope;   // cos/sin table: t band [n_t][np_t], then h [lat_h][np_h], then w [lat_w][np_w]
+  RopeGeom g;
   int32_t n_seg;
   int32_t n_q;          // T
   int32_t n_heads;
-  int32_t lat_w;
-  int32_t hw;           // tokens per frame
   int32_t q_t_index;    // temporal table row of the current block's first frame
-  int32_t np_t, np_h, np_w;   // RoPE pairs per band
-  int32_t rope_h_off, rope_w_off;  // float2 offsets of the h and w tables
-  int32_t rope_bytes;   // size of the whole cos/sin table
   int32_t n_qtiles;
   float scale_log2;     // log2(e) / sqrt(d)
-  // n / hw == umulhi(n, magic_hw) + n * one_hw and j / lat_w == umulhi(j, magic_w) +
-  // j * one_w over the token ranges used (checked on the host); a divisor of 1 has
-  // magic 0 and one 1.
-  uint32_t magic_hw, one_hw;
-  uint32_t magic_w, one_w;
 };
 
 // Bank / retrieval state kept in device memory inside the arena.
@@ -58,13 +84,33 @@ struct DevState {
   int32_t pad_[3];
 };
 
+// One RoPE-follow job: rotate raw keys [n_tok][H][d] of n_layers layers at the
+// positions of a segment whose first frame has temporal row t_index.
+struct RotJob {
+  const char* src;      // raw K of layer 0
+  char* dst;            // rotated K of layer 0; ignored when from_state
+  int64_t dst_off;      // from_state: byte offset of layer 0's rotated K inside a block slot
+  int32_t t_index;
+  int32_t from_state;   // 1: destination slot = device state's copy_dst, skipped when copy_src < 0
+};
+
+struct RotParams {
+  RotJob job[kMaxRotJobs];
+  RopeGeom g;
+  const DevState* st;
+  char* block_base;     // first block slot (from_state jobs)
+  int64_t slot_bytes;   // block slot size (from_state jobs)
+  int64_t layer_bytes;  // distance between consecutive layers, source and destination
+  int32_t n_jobs, n_tok, n_heads, head_dim, elem;
+};
+
 // Launchers (kernels_*.hip).  All return the launch status.
 hipError_t launch_attention(const AttnParams& p, int dtype, int head_dim, hipStream_t s);
+hipError_t launch_rope_follow(const RotParams& p, int n_layers, hipStream_t s);
 hipError_t launch_kv_write(const void* k_src, const void* v_src, void* k_dst0, void* v_dst0,
-                           void* k_dst1, void* v_dst1, int n_tok, int n_heads, int head_dim,
-                           int t_pad, int elem_bytes, hipStream_t s);
-hipError_t launch_slot_copy(char* block_base, size_t slot_bytes, const DevState* st,
-                            hipStream_t s);
+                           void* k_dst1, void* v_dst1, size_t bytes, hipStream_t s);
+hipError_t launch_slot_copy(char* block_base, size_t slot_bytes, size_t copy_bytes,
+                            const DevState* st, hipStream_t s);
 hipError_t launch_retrieve(const float* fp_raw, double* phi_cur, const double* bank_phi,
                            DevState* st, int fp_dim, int bank_count, int block,
                            int dyn_slot, int bank_slot0, int32_t* slot_out, hipStream_t s);

@@ -15,13 +15,17 @@
  * formula over [K_ref; history; current], retrieval, Clean KV Update, RoPE
  * follow).
  *
- * Keys are stored raw (before RoPE) and re-rotated with 3D RoPE at their
- * *current* cache position inside every attention call ("RoPE follow"; review,
- * full-pipeline and novelty paragraphs).  Temporal positions are fixed by
- * slot: Ref at t0, then Static, Dynamic, the previous window blocks (oldest
- * first) and the current block, each block_frames frames long; spatial
- * positions are the latent (row, column).  An empty segment is skipped and the
- * others keep their positions.
+ * Keys are stored raw (before RoPE) and attended rotated with 3D RoPE at their
+ * *current* cache position ("RoPE follow"; review, full-pipeline and novelty
+ * paragraphs).  Temporal positions are fixed by place: Ref at t0, then Static,
+ * Dynamic, the previous window blocks (oldest first) and the current block,
+ * each block_frames frames long; spatial positions are the latent (row,
+ * column).  An empty segment is skipped and the others keep their positions.
+ * The library rotates a block's raw keys whenever the block takes a new place
+ * (Ref at set-up, Static when block 1 opens, each window block as the window
+ * slides, a bank entry at the Dynamic place when written, the current block on
+ * every attention call) and keeps the rotated copy next to the raw keys, so a
+ * key is rotated once per place rather than once per query tile.
  *
  * Memory: the caller allocates ONE device arena of pr_sink_arena_bytes(cfg)
  * bytes and every input/output tensor.  The library never allocates or frees
@@ -126,14 +130,16 @@ int pr_sink_set_ref(pr_sink_cache* c, int32_t layer, const void* k_raw, const vo
  * ties) and copies that entry's K/V of all layers into the Dynamic Sink
  * (review, full-pipeline paragraph: r(b) = argmax phi_b . phi_i excluding b-1;
  * novelty paragraph: cosine similarity of l2-normalised fingerprints).  If no
- * entry is eligible the Dynamic Sink is not attended during this block.
+ * entry is eligible the Dynamic Sink is not attended during this block.  The
+ * copy is skipped when the entry's block already sits in the Dynamic Sink.
+ * Also re-rotates the keys of the blocks whose place changes as block opens.
  * slot_out_dev (device int32, nullable) receives the bank slot or -1. */
 int pr_sink_retrieve(pr_sink_cache* c, int32_t block, const float* fp_raw_dev,
                      int32_t* slot_out_dev, void* stream);
 
-/* One attention call of the open block for `layer`: rotates q (device,
- * [T][H][d], raw) at the current block's positions and every cached raw key at
- * its segment's current position, and writes
+/* One attention call of the open block for `layer`: rotates q and k_cur_raw
+ * (device, [T][H][d], raw) at the current block's positions, takes every
+ * cached key rotated at its segment's current position, and writes
  *   out = softmax(q_rot K_rot^T / sqrt(d)) V
  * over [Ref; Static; Dynamic; window; current] (review, full-pipeline
  * paragraph, attention formula; the current block attends to itself without
@@ -166,11 +172,14 @@ int pr_sink_bank_update(pr_sink_cache* c, int32_t block, void* stream);
 int pr_sink_bank_state(pr_sink_cache* c, int32_t* ids_host, double* fp_host,
                        int32_t* misc_host, void* stream);
 
-/* Device pointers to the raw K and V of one slot and layer, for inspection.
- * Both are [t_pad][H][d], token-major like the tensors passed in; t_pad (a
- * multiple of 64; the padding rows are zero) goes to *t_pad_out. */
+/* Device pointers to the raw K, the V and the rotated K of one slot and
+ * layer, for inspection.  All are [t_pad][H][d], token-major like the tensors
+ * passed in; t_pad (a multiple of 64; the padding rows are zero) goes to
+ * *t_pad_out.  The rotated K holds the keys rotated at the slot's place as of
+ * the last block opened (a bank entry: at the Dynamic Sink's place); k_rot_dev
+ * may be NULL. */
 int pr_sink_slot_view(const pr_sink_cache* c, int32_t slot, int32_t layer, void** k_dev,
-                      void** v_dev, int32_t* t_pad_out);
+                      void** v_dev, void** k_rot_dev, int32_t* t_pad_out);
 
 /* Segments of the open block in cache order (Ref, Static, Dynamic, W-1
  * window blocks oldest first, current): token counts (0 = not attended) and

@@ -45,6 +45,39 @@ def check_attn(out, ref, cfg, what):
     return err
 
 
+def check_rotations(cache, orc, cfg, layer, ref_k, block_k, kinds=None):
+    """RoPE follow: the rotated K the cache keeps for every attended place (and
+    for every bank entry, at the Dynamic Sink's place) equals the oracle's
+    rotation of that block's raw keys at the place's positions, to half a bf16
+    ulp (fp32: 1e-6 relative); padding rows stay zero."""
+    W = cfg.window_slots
+    segs = orc.segment_layout()
+    dyn_t = segs[2][2]
+    slot_of = {O.SEG_REF: binding.SLOT_REF, O.SEG_STATIC: binding.SLOT_STATIC,
+               O.SEG_DYNAMIC: binding.SLOT_DYNAMIC}
+    places = []
+    for kind, bid, t_start, n_frames, present in segs:
+        if not present or kind == O.SEG_CURRENT or (kinds and kind not in kinds):
+            continue
+        slot = binding.SLOT_WINDOW0 + bid % W if kind == O.SEG_WINDOW else slot_of[kind]
+        places.append((slot, bid, t_start, n_frames))
+    if not kinds or "bank" in kinds:
+        for i, bid in enumerate(orc.bank_ids):
+            places.append((cache.slot_index_bank(i), bid, dyn_t, cfg.block_frames))
+    rtol = 2.0 ** -8 * 1.001 if cfg.dtype == synth.DTYPE_BF16 else 1e-6
+    for slot, bid, t_start, n_frames in places:
+        raw = ref_k if bid is None else block_k(bid)
+        T = raw.shape[0]
+        _, _, rot = cache.slot_view(slot, layer, rotated=True)
+        got = rot[:T].float().cpu().numpy()
+        pos = O.frame_positions(n_frames, t_start, cfg.lat_h, cfg.lat_w)
+        want = O.rope_rotate(raw, pos, cfg.rope_dims, cfg.rope_theta)
+        bad = np.abs(got - want) > rtol * np.abs(want) + 1e-6 * float(np.abs(raw).max())
+        assert not bad.any(), f"slot {slot} (block {bid}, t {t_start}): {int(bad.sum())} elements off"
+        assert not rot[T:].any(), f"slot {slot}: padding rows written"
+    return len(places)
+
+
 class Stream:
     """Drives the GPU cache and the oracle side by side on seeded numpy inputs."""
 
@@ -98,6 +131,11 @@ class Stream:
             assert misc[2] == expect, f"block {b}: bank decision {misc[2]} vs {dec}"
         return dec
 
+    def check_rotations(self, layer):
+        return check_rotations(self.cache, self.orc, self.cfg, layer,
+                               synth.ref_kv(self.cfg, layer, self.seed)[0],
+                               lambda bid: self.clean(bid, layer)[0])
+
     def check_slot_bytes(self, slot, block, layer):
         """Stored raw K/V of a slot equal the block's clean K/V bit for bit; padding is zero."""
         kt, vt = self.cache.slot_view(slot, layer)
@@ -120,6 +158,7 @@ def test_c0_stream_30_blocks_fp32():
     worst = 0.0
     for b in range(30):
         st.open(b, fps[b])
+        st.check_rotations(b % cfg.n_layers)
         for l in range(cfg.n_layers):
             worst = max(worst, st.attend_check(l, step=b % 3))
         st.close(b)
@@ -149,6 +188,7 @@ def test_bf16_multitile_every_block(cfg):
     fps = synth.pose_stream(8, seed=5)
     for b in range(8):
         st.open(b, fps[b])
+        st.check_rotations((b + 1) % cfg.n_layers)
         st.attend_check(b % cfg.n_layers, step=0)
         st.close(b)
     for i, bid in enumerate(st.orc.bank_ids):
@@ -165,6 +205,7 @@ def test_bank_fill_and_freeze_with_swaps():
     for b in range(26):
         st.open(b, fps[b])
         if b in (0, 1, 2, 19, 20, 25):
+            st.check_rotations(0)
             st.attend_check(0)
         dec = st.close(b)
         swaps += dec is not None and dec[0] == "swap"
@@ -228,6 +269,10 @@ def test_full_size_sampled_parity(name, cfg, b, seed):
     # same call again: bitwise identical
     out2 = cache.attend(0, q, kc, vc)
     assert torch.equal(out, out2)
+    # RoPE follow after the window has slid: window blocks and the Dynamic Sink
+    n = check_rotations(cache, orc, cfg, 0, None, lambda bid: host(kv_of(bid, 0)[0]),
+                        kinds=(O.SEG_WINDOW, O.SEG_DYNAMIC))
+    assert n == 3
 
 
 def test_ring_phase_bitwise_invariance():
