@@ -72,10 +72,19 @@ __device__ inline uint32_t lds_addr(const char* p) {
 
 // 16 bytes per lane from a buffer resource into LDS: lane i writes
 // M0 + 16 i.  The load is invisible to the compiler's counters; callers wait
-// on vmcnt themselves.
+// on vmcnt themselves.  M0 is saved and restored around it, and the LDS DMA
+// issues one wait state after the M0 write (the gfx9 M0 -> LDS-DMA hazard).
 __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t lds, uint32_t voff) {
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-               :: "s"(lds), "v"(voff), "s"(r) : "memory", "m0");
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds), "v"(voff), "s"(r)
+      : "memory");
 }
 
 // s_waitcnt vmcnt(n), other counters untouched (gfx9 encoding).
@@ -85,23 +94,38 @@ __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt(0x3f70 | (N & 15) | ((N >> 4) << 14));
 }
 
-// Walks the full 64-key tiles in segment order.
+// Walks the full 64-key tiles of one head in segment order: k / v point at
+// the next tile's first key, `left` counts the full tiles still to come in the
+// current segment.  Moving to the next segment (the only scalar loads) happens
+// a handful of times per workgroup.
 struct TileCursor {
-  int s, n0;
-  __device__ void first(const AttnParams& p) {
-    s = 0;
-    n0 = 0;
+  const char* k;
+  const char* v;
+  int left, s;
+  __device__ __forceinline__ void seek(const AttnParams& p, size_t head_off) {
     while (s < p.n_seg && p.seg[s].count < kKeyTile) ++s;
+    if (s < p.n_seg) {
+      k = static_cast<const char*>(p.seg[s].k) + head_off;
+      v = static_cast<const char*>(p.seg[s].v) + head_off;
+      left = p.seg[s].count / kKeyTile;
+    }
   }
-  __device__ void next(const AttnParams& p) {
-    n0 += kKeyTile;
-    if (s < p.n_seg && n0 + kKeyTile > p.seg[s].count) {
+  __device__ __forceinline__ void first(const AttnParams& p, size_t head_off) {
+    s = 0;
+    k = v = static_cast<const char*>(p.seg[0].k);
+    left = 0;
+    seek(p, head_off);
+  }
+  __device__ __forceinline__ void next(const AttnParams& p, size_t head_off, uint32_t tile_bytes) {
+    k += tile_bytes;
+    v += tile_bytes;
+    if (__builtin_expect(--left == 0, 0)) {
       ++s;
-      n0 = 0;
-      while (s < p.n_seg && p.seg[s].count < kKeyTile) ++s;
+      seek(p, head_off);
     }
   }
 };
+
 
 template <int D>
 struct Attn {
@@ -202,6 +226,12 @@ struct Attn {
                                            0, nrec, kBufferConfig);
     rv = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(static_cast<const char*>(sg.v) + off),
                                            0, nrec, kBufferConfig);
+  }
+
+  // Buffer resource of a full tile starting at `base` (valid) or an empty one.
+  __device__ __forceinline__ __amdgpu_buffer_rsrc_t full_rsrc(const char* base, bool valid) const {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), 0,
+                                             valid ? (int)(KT * tok_bytes) : 0, kBufferConfig);
   }
 
   // This wave's share (NDMA instructions) of a K or V tile into LDS.
@@ -314,6 +344,53 @@ struct Attn {
     pv_half(vt, 1, pb);
   }
 
+  // ---- steady-state schedule -------------------------------------------
+  // One iteration (QK^T of the next tile, PV of the current one) is a fixed
+  // sequence of NOPS steps in four groups: A = QK^T keys 0..31 (NC steps),
+  // B = PV keys 0..31 (2*NDB steps), C = QK^T keys 32..63, D = PV keys 32..63.
+  // Each step issues the LDS read of the operand two steps ahead, its two
+  // MFMAs (one per query block), and PAIRS packed softmax pairs; steps are
+  // fenced, so this order is the issue order.
+  static constexpr int GA = NC, GB = 2 * NDB;
+  static constexpr int NOPS = 2 * GA + 2 * GB;
+  static constexpr int PAIRS = 8 / GA;  // softmax pairs per step (GA == GB)
+  static_assert(GA == GB, "groups of equal length");
+
+  // MFMA A operand t of an iteration (t >= NOPS: the next iteration's first
+  // operands, from the next K tile).
+  __device__ __forceinline__ bf16x8 op(int t, const char* kt, const char* vt, const char* kn) const {
+    if (t >= NOPS) return *reinterpret_cast<const bf16x8*>(kn + l32 * RBP + hh * 16 + (t - NOPS) * 32);
+    const int g = t / GA, i = t % GA;
+    if (g == 0 || g == 2) {  // K, key block g/2, k-step i
+      return *reinterpret_cast<const bf16x8*>(kt + ((g / 2) * 32 + l32) * RBP + hh * 16 + i * 32);
+    }
+    // V^T, dv block i/2, k-step kc = 2*(g/2) + i%2
+    const int db = i / 2, kc = 2 * (g / 2) + i % 2;
+    const int grp = lane >> 4, i16 = lane & 15;
+    const char* vl = vt + (8 * hh + (i16 >> 2)) * RBP + (16 * (grp & 1) + 4 * (i16 & 3)) * 2;
+    i16x4 h[2];
+#pragma unroll
+    for (int rd = 0; rd < 2; ++rd)
+      h[rd] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) i16x4*)(vl + (16 * kc + 4 * rd) * RBP + 64 * db));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(h[0], h[1], 0, 1, 2, 3, 4, 5, 6, 7));
+  }
+
+  // Packed softmax pair e (elements 2e, 2e+1) of a 16-score block already
+  // shifted by -m: returns the packed bf16 word, adds its sum to acc.  The
+  // empty asm keeps the work in the step that issues it (the compiler would
+  // otherwise sink it next to its first use, a whole group later).
+  __device__ __forceinline__ uint32_t soft_pair(const f32x16& s, int e, float& acc) const {
+    uint32_t w = pack_bf16(__builtin_amdgcn_exp2f(s[2 * e]), __builtin_amdgcn_exp2f(s[2 * e + 1]));
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), kOnes, acc, false);
+    asm volatile("" : "+v"(w), "+v"(acc));
+    return w;
+  }
+
+  static __device__ __forceinline__ bf16x8 words(const uint32_t (&w)[4]) {
+    return __builtin_bit_cast(bf16x8, make_uint4(w[0], w[1], w[2], w[3]));
+  }
+
   __device__ void epilogue(int qt) {
     // register 4g+e of dv block db is dv = 32db + 8g + 4hh + e
 #pragma unroll
@@ -353,26 +430,24 @@ void attn_bf16_kernel(const AttnParams p) {
   bool bad = false;
   if (n_full > 0) {
     // K and V of tile t go to stage t % 3.  DMA groups: K0 alone, then
-    // {K1, V0}, {K2, V1}, and iteration j issues {K(j+3), V(j+2)}, so at the
-    // top of iteration j a wave waits for all but its newest group.  Tiles past
-    // the last one load as zeros into stages nobody reads.
+    // {K1, V0}, {K2, V1}; iteration j issues {K(j+3), V(j+2)} after its
+    // barrier, which waits for every earlier group.  Tiles past the last one
+    // load as zeros into stages nobody reads.
+    const size_t head_off = (size_t)head * D * 2;
+    const uint32_t tile_bytes = A::KT * a.tok_bytes;
     TileCursor ck, cv;  // next K tile to load, next V tile to load
-    ck.first(p);
+    ck.first(p, head_off);
     cv = ck;
     int kt_next = 0, vt_next = 0;
     auto load_k = [&]() {
-      __amdgpu_buffer_rsrc_t rk, rv;
-      a.rsrc(ck.s, ck.n0, kt_next < n_full, rk, rv);
-      a.dma_k(a.kbuf(kt_next % A::STAGES), rk);
+      a.dma_k(a.kbuf(kt_next % A::STAGES), a.full_rsrc(ck.k, kt_next < n_full));
       ++kt_next;
-      ck.next(p);
+      ck.next(p, head_off, tile_bytes);
     };
     auto load_v = [&]() {
-      __amdgpu_buffer_rsrc_t rk, rv;
-      a.rsrc(cv.s, cv.n0, vt_next < n_full, rk, rv);
-      a.dma_v(a.vbuf(vt_next % A::STAGES), rv);
+      a.dma_v(a.vbuf(vt_next % A::STAGES), a.full_rsrc(cv.v, vt_next < n_full));
       ++vt_next;
-      cv.next(p);
+      cv.next(p, head_off, tile_bytes);
     };
     load_k();  // K0
     a.init_queries(qt);
@@ -380,7 +455,7 @@ void attn_bf16_kernel(const AttnParams p) {
     load_v();  // V0
     load_k();  // K2
     load_v();  // V1
-    wait_vm<4 * A::NDMA>();  // K0 landed
+    wait_vm<2 * A::NDMA>();  // K0, K1 and V0 landed
     __syncthreads();
 
     // First tile, exact: sets each row's reference max m.
@@ -407,40 +482,99 @@ void attn_bf16_kernel(const AttnParams p) {
     float l0 = a.soft(s_lo[0], pb[0][0], pb[0][1]);
     float l1 = a.soft(s_lo[1], pb[1][0], pb[1][1]);
 
-    // Steady state: iteration j = QK^T of tile j+1 and PV of tile j.
-    // Entering it, pb[.][0..1] (keys 0..31 of tile j) and s_hi (keys 32..63
-    // of tile j, already shifted by -m) are ready.
+    // Steady state: iteration j = QK^T of tile j+1 and PV of tile j, in the
+    // fixed step order of Attn::NOPS.  Entering it: pw[.][0..1] (P of keys
+    // 0..31 of tile j), s_hi (scores of keys 32..63 of tile j, shifted by -m)
+    // and the first two K operands of tile j+1 are ready.  The one barrier of
+    // an iteration sits between groups B and C: it waits for the DMA group
+    // issued an iteration earlier ({K(j+2), V(j+1)}), so the next tile's first
+    // operands can be read before the iteration ends; then the group
+    // {K(j+3), V(j+2)} is issued, one DMA per step of groups C and D.
+    uint32_t pw[2][4][4];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+      for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) pw[qb][kc][w] = __builtin_bit_cast(uint4, pb[qb][kc])[w];
+    // operand t of an iteration lives in ring[t % 4]; 4 divides NOPS, so the
+    // slots line up from one iteration to the next
+    static_assert(A::NOPS % 4 == 0, "operand ring");
+    bf16x8 ring[4];
+    {
+      const char* kt = a.kbuf(1 % A::STAGES);
+      ring[0] = a.op(A::NOPS, kt, kt, kt);
+      ring[1] = a.op(A::NOPS + 1, kt, kt, kt);
+    }
     for (int j = 0; j + 1 < n_full; ++j) {
-      wait_vm<2 * A::NDMA>();  // K(j+1) and V(j) landed (own share)
-      __syncthreads();         // ... everyone's share; stages of K(j), V(j-1) free
-      load_k();                // K(j+3)
-      load_v();                // V(j+2)
       const char* kt = a.kbuf((j + 1) % A::STAGES);
       const char* vt = a.vbuf(j % A::STAGES);
+      const char* kn = a.kbuf((j + 2) % A::STAGES);
       f32x16 n_lo[2], n_hi[2];
-      a.qk_half(kt, 0, cm, n_lo);
-      l0 += a.soft(s_hi[0], pb[0][2], pb[0][3]);
-      a.pv_half(vt, 0, pb);
-      l1 += a.soft(s_hi[1], pb[1][2], pb[1][3]);
-      a.qk_half(kt, 1, cm, n_hi);
-      bf16x8 nb[2][2];
-      l0 += a.soft(n_lo[0], nb[0][0], nb[0][1]);
-      a.pv_half(vt, 1, pb);
-      l1 += a.soft(n_lo[1], nb[1][0], nb[1][1]);
+      uint32_t nw[2][2][4];
+      __amdgpu_buffer_rsrc_t rk, rv;
+      uint32_t lk = 0, lv = 0;
+#pragma unroll
+      for (int t = 0; t < A::NOPS; ++t) {
+        const int g = t / A::GA, i = t % A::GA;
+        if (t == 2 * A::GA) {  // between groups B and C
+          wait_vm<0>();
+          __syncthreads();
+          rk = a.full_rsrc(ck.k, kt_next < n_full);
+          rv = a.full_rsrc(cv.v, vt_next < n_full);
+          lk = lds_addr(a.kbuf(kt_next % A::STAGES)) + a.wave * A::NDMA * 1024;
+          lv = lds_addr(a.vbuf(vt_next % A::STAGES)) + a.wave * A::NDMA * 1024;
+          ++kt_next;
+          ++vt_next;
+          ck.next(p, head_off, tile_bytes);
+          cv.next(p, head_off, tile_bytes);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        ring[(t + 2) % 4] = a.op(t + 2, kt, vt, kn);
+        const bf16x8 x = ring[t % 4];
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+          if (g == 0) n_lo[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x, a.qreg[qb][i], i == 0 ? cm[qb] : n_lo[qb], 0, 0, 0);
+          if (g == 2) n_hi[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x, a.qreg[qb][i], i == 0 ? cm[qb] : n_hi[qb], 0, 0, 0);
+          if (g == 1 || g == 3) {
+            const int db = i / 2, kc = 2 * (g / 2) + i % 2;
+            a.o[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x, A::words(pw[qb][kc]), a.o[qb][db], 0, 0, 0);
+          }
+        }
+#pragma unroll
+        for (int e = i * A::PAIRS; e < (i + 1) * A::PAIRS; ++e) {
+          if (g == 0) pw[0][2 + e / 4][e % 4] = a.soft_pair(s_hi[0], e, l0);
+          if (g == 1) pw[1][2 + e / 4][e % 4] = a.soft_pair(s_hi[1], e, l1);
+          if (g == 2) nw[0][e / 4][e % 4] = a.soft_pair(n_lo[0], e, l0);
+          if (g == 3) nw[1][e / 4][e % 4] = a.soft_pair(n_lo[1], e, l1);
+        }
+        if (g == 2 && i < A::NDMA) dma16(rk, lk + i * 1024, a.voff_k[i]);
+        if (g == 3 && i < A::NDMA) dma16(rv, lv + i * 1024, a.voff_v[i]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
         s_hi[qb] = n_hi[qb];
-        pb[qb][0] = nb[qb][0];
-        pb[qb][1] = nb[qb][1];
+#pragma unroll
+        for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+          for (int w = 0; w < 4; ++w) pw[qb][kc][w] = nw[qb][kc][w];
       }
     }
-    // Drain: PV of the last full tile.
-    wait_vm<2 * A::NDMA>();
+    // Drain: PV of the last full tile (its V arrived with an earlier group).
+    wait_vm<0>();
     __syncthreads();
     {
       const char* vt = a.vbuf((n_full - 1) % A::STAGES);
-      l0 += a.soft(s_hi[0], pb[0][2], pb[0][3]);
-      l1 += a.soft(s_hi[1], pb[1][2], pb[1][3]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        pw[0][2 + e / 4][e % 4] = a.soft_pair(s_hi[0], e, l0);
+        pw[1][2 + e / 4][e % 4] = a.soft_pair(s_hi[1], e, l1);
+      }
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int kc = 0; kc < 4; ++kc) pb[qb][kc] = A::words(pw[qb][kc]);
       a.pv_half(vt, 0, pb);
       a.pv_half(vt, 1, pb);
     }
