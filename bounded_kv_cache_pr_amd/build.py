@@ -28,6 +28,8 @@ def compile_command(out_path: str, extra=()) -> list:
         hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
         # packed fp32 VALU ops stay off: ordinary float code only
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        # the attention loop's fenced step sequence is unrolled in full
+        "-mllvm", "-pragma-unroll-threshold=1000000",
         "-I", INCLUDE, "-I", CSRC,
         *[os.path.join(CSRC, s) for s in SOURCES],
         *extra,

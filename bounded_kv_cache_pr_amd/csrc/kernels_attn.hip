@@ -31,6 +31,8 @@
 // The fp32 kernel is a plain one-query-per-lane loop for fp32 caches.
 #include "prsink_internal.h"
 
+#include <type_traits>
+
 namespace prsink {
 namespace {
 
@@ -40,7 +42,6 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) char lds_char;
 
-__device__ constexpr bf16x2 kOnes = {(__bf16)1.0f, (__bf16)1.0f};
 
 // Fourth dword of a gfx9 raw buffer resource (32-bit data format).
 constexpr int kBufferConfig = 0x00020000;
@@ -94,6 +95,23 @@ __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt(0x3f70 | (N & 15) | ((N >> 4) << 14));
 }
 
+// QK^T MFMAs of the steady-state loop, with the scores accumulating in VGPRs
+// and the query operand read from AGPRs.  (The compiler gives every MFMA of a
+// function one register form; the PV MFMAs keep O in AGPRs, and a VALU read
+// of an AGPR next to running MFMAs costs several cycles, so the scores the
+// softmax reads live in VGPRs.)  The loop reads a score no sooner than nine
+// steps (18 MFMAs) after the MFMA that wrote it, well past the wait states an
+// MFMA result needs before a VALU read; the accumulating MFMA has its source
+// C tied to its destination, the case the hardware chains back to back.
+__device__ __forceinline__ f32x16 mfma_qk_first(bf16x8 a, bf16x8 b, const f32x16& c) {
+  f32x16 d;
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %3" : "=&v"(d) : "v"(a), "a"(b), "v"(c));
+  return d;
+}
+__device__ __forceinline__ void mfma_qk_acc(f32x16& d, bf16x8 a, bf16x8 b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "a"(b));
+}
+
 // Walks the full 64-key tiles of one head in segment order: k / v point at
 // the next tile's first key, `left` counts the full tiles still to come in the
 // current segment.  Moving to the next segment (the only scalar loads) happens
@@ -138,9 +156,12 @@ struct Attn {
   // banks once.
   static constexpr int RBP = D == 128 ? RB + 48 : RB + 16;
   static constexpr int NU = RBP / 16;    // 16-byte units per padded row
-  static constexpr int NDMA = (KT * NU + 255) / 256;  // DMA instructions per wave, tile and tensor
-  static constexpr int TILE = NDMA * 4 * 1024;        // bytes per tile buffer (tail slack included)
-  static constexpr int STAGES = 3;
+  static constexpr int UNITS = KT * NU;  // 16-byte units of one LDS tile
+  static constexpr int NDMA = (UNITS + 255) / 256;  // DMA instructions per wave, tile and tensor
+  static constexpr int TILE = KT * RBP;  // bytes per tile buffer
+  static constexpr int STAGES = 4;
+  static constexpr int LDS_BYTES = 2 * STAGES * TILE + 1024;  // K stages, V stages, DMA sink
+  static_assert(UNITS % 64 == 0, "a DMA instruction never straddles the end of a tile");
   static constexpr int NC = D / 16;      // QK^T k-steps
   static constexpr int NDB = D / 32;     // dv blocks
   static constexpr float SUM_LIMIT = 18446744073709551616.0f;  // 2^64
@@ -176,6 +197,14 @@ struct Attn {
 
   __device__ char* kbuf(int st) const { return smem + st * TILE; }
   __device__ char* vbuf(int st) const { return smem + (STAGES + st) * TILE; }
+
+  // LDS destination of this wave's DMA instruction i into `tile`.  The four
+  // waves issue NDMA instructions each; an instruction that falls wholly past
+  // the tile (all its lanes are padding and load zeros) goes to a 1 KB sink.
+  __device__ __forceinline__ uint32_t dma_lds(const char* tile, int i) const {
+    const int u0 = (wave * NDMA + i) * 64;
+    return u0 < UNITS ? lds_addr(tile) + u0 * 16 : lds_addr(smem + 2 * STAGES * TILE);
+  }
 
   // Q' = bf16(rot(q) * log2(e)/sqrt(d)) as the QK^T B operand.
   __device__ void init_queries(int qt) {
@@ -236,14 +265,12 @@ struct Attn {
 
   // This wave's share (NDMA instructions) of a K or V tile into LDS.
   __device__ __forceinline__ void dma_k(char* dst, __amdgpu_buffer_rsrc_t r) const {
-    const uint32_t base = lds_addr(dst) + wave * NDMA * 1024;
 #pragma unroll
-    for (int i = 0; i < NDMA; ++i) dma16(r, base + i * 1024, voff_k[i]);
+    for (int i = 0; i < NDMA; ++i) dma16(r, dma_lds(dst, i), voff_k[i]);
   }
   __device__ __forceinline__ void dma_v(char* dst, __amdgpu_buffer_rsrc_t r) const {
-    const uint32_t base = lds_addr(dst) + wave * NDMA * 1024;
 #pragma unroll
-    for (int i = 0; i < NDMA; ++i) dma16(r, base + i * 1024, voff_v[i]);
+    for (int i = 0; i < NDMA; ++i) dma16(r, dma_lds(dst, i), voff_v[i]);
   }
 
   // S'^T of key block kb (32 keys) for both query blocks; the accumulators
@@ -264,17 +291,16 @@ struct Attn {
   // as the PV B operands of k-steps 2kb and 2kb+1 (register r holds key
   // 16*(r/8) + 8hh + r%8 of the block); returns the lane's sum of the packed
   // values, so the normaliser sums the same rounded weights the PV uses.
-  __device__ __forceinline__ float soft(const f32x16& s, bf16x8& p_lo, bf16x8& p_hi) const {
+  __device__ __forceinline__ void soft(const f32x16& s, bf16x8& p_lo, bf16x8& p_hi, float& acc) const {
     uint32_t pw[8];
-    float acc = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       pw[e] = pack_bf16(__builtin_amdgcn_exp2f(s[2 * e]), __builtin_amdgcn_exp2f(s[2 * e + 1]));
-      acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw[e]), kOnes, acc, false);
+      acc += __uint_as_float(pw[e] << 16);
+      acc += __uint_as_float(pw[e] & 0xffff0000u);
     }
     p_lo = __builtin_bit_cast(bf16x8, make_uint4(pw[0], pw[1], pw[2], pw[3]));
     p_hi = __builtin_bit_cast(bf16x8, make_uint4(pw[4], pw[5], pw[6], pw[7]));
-    return acc;
   }
 
   // O^T += V^T P^T over keys 32kb .. 32kb+31.  Lane (dv = 32db + l32, hh) needs
@@ -336,7 +362,7 @@ struct Attn {
         f32x16 t = sc[kb][qb];
 #pragma unroll
         for (int r = 0; r < 16; ++r) t[r] -= m_new;
-        rs += soft(t, pb[qb][2 * kb], pb[qb][2 * kb + 1]);
+        soft(t, pb[qb][2 * kb], pb[qb][2 * kb + 1], rs);
       }
       l_run[qb] = l_run[qb] * alpha + rs;
     }
@@ -348,7 +374,7 @@ struct Attn {
   // One iteration (QK^T of the next tile, PV of the current one) is a fixed
   // sequence of NOPS steps in four groups: A = QK^T keys 0..31 (NC steps),
   // B = PV keys 0..31 (2*NDB steps), C = QK^T keys 32..63, D = PV keys 32..63.
-  // Each step issues the LDS read of the operand two steps ahead, its two
+  // Each step issues the LDS read of the operand three steps ahead, its two
   // MFMAs (one per query block), and PAIRS packed softmax pairs; steps are
   // fenced, so this order is the issue order.
   static constexpr int GA = NC, GB = 2 * NDB;
@@ -377,12 +403,15 @@ struct Attn {
   }
 
   // Packed softmax pair e (elements 2e, 2e+1) of a 16-score block already
-  // shifted by -m: returns the packed bf16 word, adds its sum to acc.  The
-  // empty asm keeps the work in the step that issues it (the compiler would
-  // otherwise sink it next to its first use, a whole group later).
+  // shifted by -m: returns the packed bf16 word, adds its two (rounded)
+  // values to acc.  The sum uses shifts and fp32 adds: a v_dot2 between MFMAs
+  // stalls the matrix pipe for far longer.  The empty asm keeps the work in
+  // the step that issues it (the compiler would otherwise sink it next to its
+  // first use, a whole group later).
   __device__ __forceinline__ uint32_t soft_pair(const f32x16& s, int e, float& acc) const {
     uint32_t w = pack_bf16(__builtin_amdgcn_exp2f(s[2 * e]), __builtin_amdgcn_exp2f(s[2 * e + 1]));
-    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), kOnes, acc, false);
+    acc += __uint_as_float(w << 16);
+    acc += __uint_as_float(w & 0xffff0000u);
     asm volatile("" : "+v"(w), "+v"(acc));
     return w;
   }
@@ -413,11 +442,104 @@ struct Attn {
   }
 };
 
+// Software-pipelined softmax of the steady-state loop (see the kernel).  Pair
+// q (0..31) of an iteration is exponentiated at step q / PAIRS (stage 0) and
+// packed to bf16 and summed one step later (stage 1), in the next iteration
+// when that passes the end.  Exponentials move between the stages through a
+// two-slot ring indexed by the parity of the stage-0 step (NOPS is even, so
+// the parity survives the wrap).
+template <class A>
+struct SoftPipe {
+  static constexpr int NOPS = A::NOPS, PAIRS = A::PAIRS, NSTAGE = 2;
+  static_assert(NOPS % 2 == 0, "the stage ring is indexed by step parity");
+  f32x16 s_hi[2];         // scores of keys 32..63 of the current tile, shifted by -m
+  uint32_t pw[2][4][4];   // PV B operands [query block][k-step][word]
+  uint32_t nw[2][2][4];   // words of the next tile's keys 0..31 made in this iteration
+  float e[2][PAIRS][2];
+  float acc[2][2];        // row sums [query block][even/odd element]
+
+  __device__ void init(const bf16x8 (&pb)[2][4], float l0, float l1, const f32x16 (&sh)[2]) {
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      s_hi[qb] = sh[qb];
+#pragma unroll
+      for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) pw[qb][kc][w] = __builtin_bit_cast(uint4, pb[qb][kc])[w];
+    }
+    acc[0][0] = l0;
+    acc[1][0] = l1;
+    acc[0][1] = acc[1][1] = 0.f;
+  }
+
+  // The packed word of pair q: pairs 0..15 feed k-steps 2..3 of this tile;
+  // pairs 16..31 feed k-steps 0..1 of the next tile, held in nw while made
+  // within their iteration and in pw once the next iteration has begun.
+  __device__ __forceinline__ uint32_t& word(int q, bool next) {
+    if (q < 16) return pw[q / 8][2 + (q % 8) / 4][q % 4];
+    const int u = q - 16;
+    return next ? pw[u / 8][(u % 8) / 4][u % 4] : nw[u / 8][(u % 8) / 4][u % 4];
+  }
+
+  // Stages due at step t.  FIRST: no earlier iteration (skip wrapped stages).
+  // FLUSH: only the wrapped stages (the step after the last iteration).
+  template <bool FIRST, bool FLUSH>
+  __device__ __forceinline__ void run(int t, const f32x16& n_lo0, const f32x16& n_lo1) {
+#pragma unroll
+    for (int k = NSTAGE - 1; k >= 0; --k) {
+      const int s0 = t - k;
+      const bool wrapped = s0 < 0;
+      if ((wrapped && FIRST) || (!wrapped && FLUSH)) continue;
+      const int sl = (s0 + NOPS) & 1;
+#pragma unroll
+      for (int pp = 0; pp < PAIRS; ++pp) {
+        const int q = (wrapped ? s0 + NOPS : s0) * PAIRS + pp;
+        if (k == 0) {
+          const f32x16& sv = q < 8 ? s_hi[0] : q < 16 ? s_hi[1] : q < 24 ? n_lo0 : n_lo1;
+          e[sl][pp][0] = __builtin_amdgcn_exp2f(sv[2 * (q % 8)]);
+          e[sl][pp][1] = __builtin_amdgcn_exp2f(sv[2 * (q % 8) + 1]);
+          asm volatile("" : "+v"(e[sl][pp][0]), "+v"(e[sl][pp][1]));
+        } else {
+          uint32_t& w = word(q, wrapped);
+          w = pack_bf16(e[sl][pp][0], e[sl][pp][1]);
+          const int qb = (q / 8) & 1;
+          acc[qb][0] += e[sl][pp][0];
+          acc[qb][1] += e[sl][pp][1];
+          asm volatile("" : "+v"(w), "+v"(acc[qb][0]), "+v"(acc[qb][1]));
+        }
+      }
+    }
+  }
+
+  template <bool FIRST>
+  __device__ __forceinline__ void step(int t, const f32x16& n_lo0, const f32x16& n_lo1) {
+    run<FIRST, false>(t, n_lo0, n_lo1);
+  }
+
+  // Closes an iteration: the new keys 32..63 become s_hi, and the words made
+  // within it move to their next-iteration place.
+  __device__ __forceinline__ void end_iteration(const f32x16 (&n_hi)[2]) {
+    s_hi[0] = n_hi[0];
+    s_hi[1] = n_hi[1];
+#pragma unroll
+    for (int q = 16; q < 32; ++q)
+      if (q / PAIRS + 1 < NOPS) word(q, true) = word(q, false);
+  }
+
+  // Runs the stages still pending after the last iteration.
+  __device__ __forceinline__ void flush() {
+#pragma unroll
+    for (int t = 0; t < NSTAGE - 1; ++t) run<false, true>(t, s_hi[0], s_hi[1]);  // no reads
+  }
+
+  __device__ __forceinline__ float sum(int qb) const { return acc[qb][0] + acc[qb][1]; }
+};
+
 template <int D>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void attn_bf16_kernel(const AttnParams p) {
   using A = Attn<D>;
-  __shared__ __align__(16) char smem[2 * A::STAGES * A::TILE];
+  __shared__ __align__(16) char smem[A::LDS_BYTES];
   __shared__ int bad_flag[4];
 
   int head, qt;
@@ -429,10 +551,11 @@ void attn_bf16_kernel(const AttnParams p) {
 
   bool bad = false;
   if (n_full > 0) {
-    // K and V of tile t go to stage t % 3.  DMA groups: K0 alone, then
-    // {K1, V0}, {K2, V1}; iteration j issues {K(j+3), V(j+2)} after its
-    // barrier, which waits for every earlier group.  Tiles past the last one
-    // load as zeros into stages nobody reads.
+    // K and V of tile t go to stage t % 4.  DMA groups: K0 alone, then
+    // {K1, V0}, {K2, V1}, {K3, V2}; iteration j issues {K(j+4), V(j+3)} after
+    // its barrier, which waits for every group but the newest (two iterations
+    // of latency).  Tiles past the last one load as zeros into stages nobody
+    // reads.
     const size_t head_off = (size_t)head * D * 2;
     const uint32_t tile_bytes = A::KT * a.tok_bytes;
     TileCursor ck, cv;  // next K tile to load, next V tile to load
@@ -455,7 +578,9 @@ void attn_bf16_kernel(const AttnParams p) {
     load_v();  // V0
     load_k();  // K2
     load_v();  // V1
-    wait_vm<2 * A::NDMA>();  // K0, K1 and V0 landed
+    load_k();  // K3
+    load_v();  // V2
+    wait_vm<4 * A::NDMA>();  // K0, K1 and V0 landed
     __syncthreads();
 
     // First tile, exact: sets each row's reference max m.
@@ -479,104 +604,111 @@ void attn_bf16_kernel(const AttnParams p) {
       }
     }
     bf16x8 pb[2][4];
-    float l0 = a.soft(s_lo[0], pb[0][0], pb[0][1]);
-    float l1 = a.soft(s_lo[1], pb[1][0], pb[1][1]);
+    float l0 = 0.f, l1 = 0.f;
+    a.soft(s_lo[0], pb[0][0], pb[0][1], l0);
+    a.soft(s_lo[1], pb[1][0], pb[1][1], l1);
 
     // Steady state: iteration j = QK^T of tile j+1 and PV of tile j, in the
     // fixed step order of Attn::NOPS.  Entering it: pw[.][0..1] (P of keys
     // 0..31 of tile j), s_hi (scores of keys 32..63 of tile j, shifted by -m)
-    // and the first two K operands of tile j+1 are ready.  The one barrier of
+    // and the first three K operands of tile j+1 are ready.  The one barrier of
     // an iteration sits between groups B and C: it waits for the DMA group
-    // issued an iteration earlier ({K(j+2), V(j+1)}), so the next tile's first
+    // issued two iterations earlier ({K(j+2), V(j+1)}), so the next tile's first
     // operands can be read before the iteration ends; then the group
-    // {K(j+3), V(j+2)} is issued, one DMA per step of groups C and D.
-    uint32_t pw[2][4][4];
+    // {K(j+4), V(j+3)} is issued, one DMA per step of groups C and D.
+    //
+    // Softmax runs as a five-stage software pipeline over the 32 packed pairs
+    // of an iteration (pairs 0..7: s_hi of query block 0, 8..15: s_hi of block
+    // 1, 16..23 / 24..31: the new keys 0..31 of blocks 0 / 1): stage k of
+    // pair q runs PAIRS-per-step k steps after its read, so no instruction
+    // waits on a result issued in the same step and the MFMAs keep issuing.
+    // Stages: 0 read the scores, 1 exp2, 2 pack to bf16 (the PV operand word),
+    // 3 unpack the rounded halves, 4 add them to the row sums.  The last
+    // stages of an iteration's final pairs run in the next iteration's first
+    // steps (or in the drain).
+    SoftPipe<A> sp;
+    sp.init(pb, l0, l1, s_hi);
+    // queries live in AGPRs from here on (the QK^T MFMAs read them there)
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-      for (int kc = 0; kc < 2; ++kc)
-#pragma unroll
-        for (int w = 0; w < 4; ++w) pw[qb][kc][w] = __builtin_bit_cast(uint4, pb[qb][kc])[w];
-    // operand t of an iteration lives in ring[t % 4]; 4 divides NOPS, so the
-    // slots line up from one iteration to the next
-    static_assert(A::NOPS % 4 == 0, "operand ring");
+      for (int c = 0; c < A::NC; ++c) asm volatile("" : "+a"(a.qreg[qb][c]));
     bf16x8 ring[4];
     {
       const char* kt = a.kbuf(1 % A::STAGES);
       ring[0] = a.op(A::NOPS, kt, kt, kt);
       ring[1] = a.op(A::NOPS + 1, kt, kt, kt);
+      ring[2] = a.op(A::NOPS + 2, kt, kt, kt);
     }
-    for (int j = 0; j + 1 < n_full; ++j) {
+    auto iteration = [&](int j, auto first) {
+      constexpr bool FIRST = decltype(first)::value;
       const char* kt = a.kbuf((j + 1) % A::STAGES);
       const char* vt = a.vbuf(j % A::STAGES);
       const char* kn = a.kbuf((j + 2) % A::STAGES);
       f32x16 n_lo[2], n_hi[2];
-      uint32_t nw[2][2][4];
       __amdgpu_buffer_rsrc_t rk, rv;
-      uint32_t lk = 0, lv = 0;
+      const char* ktile = nullptr;
+      const char* vtile = nullptr;
 #pragma unroll
       for (int t = 0; t < A::NOPS; ++t) {
         const int g = t / A::GA, i = t % A::GA;
         if (t == 2 * A::GA) {  // between groups B and C
-          wait_vm<0>();
+          wait_vm<2 * A::NDMA>();
           __syncthreads();
           rk = a.full_rsrc(ck.k, kt_next < n_full);
           rv = a.full_rsrc(cv.v, vt_next < n_full);
-          lk = lds_addr(a.kbuf(kt_next % A::STAGES)) + a.wave * A::NDMA * 1024;
-          lv = lds_addr(a.vbuf(vt_next % A::STAGES)) + a.wave * A::NDMA * 1024;
+          ktile = a.kbuf(kt_next % A::STAGES);
+          vtile = a.vbuf(vt_next % A::STAGES);
           ++kt_next;
           ++vt_next;
           ck.next(p, head_off, tile_bytes);
           cv.next(p, head_off, tile_bytes);
           __builtin_amdgcn_sched_barrier(0);
         }
-        ring[(t + 2) % 4] = a.op(t + 2, kt, vt, kn);
+        ring[(t + 3) % 4] = a.op(t + 3, kt, vt, kn);
         const bf16x8 x = ring[t % 4];
+        sp.template step<FIRST>(t, n_lo[0], n_lo[1]);
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
-          if (g == 0) n_lo[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x, a.qreg[qb][i], i == 0 ? cm[qb] : n_lo[qb], 0, 0, 0);
-          if (g == 2) n_hi[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x, a.qreg[qb][i], i == 0 ? cm[qb] : n_hi[qb], 0, 0, 0);
+          if (g == 0) {
+            if (i == 0) n_lo[qb] = mfma_qk_first(x, a.qreg[qb][i], cm[qb]);
+            else mfma_qk_acc(n_lo[qb], x, a.qreg[qb][i]);
+          }
+          if (g == 2) {
+            if (i == 0) n_hi[qb] = mfma_qk_first(x, a.qreg[qb][i], cm[qb]);
+            else mfma_qk_acc(n_hi[qb], x, a.qreg[qb][i]);
+          }
           if (g == 1 || g == 3) {
             const int db = i / 2, kc = 2 * (g / 2) + i % 2;
-            a.o[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x, A::words(pw[qb][kc]), a.o[qb][db], 0, 0, 0);
+            a.o[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x, A::words(sp.pw[qb][kc]), a.o[qb][db], 0, 0, 0);
           }
         }
-#pragma unroll
-        for (int e = i * A::PAIRS; e < (i + 1) * A::PAIRS; ++e) {
-          if (g == 0) pw[0][2 + e / 4][e % 4] = a.soft_pair(s_hi[0], e, l0);
-          if (g == 1) pw[1][2 + e / 4][e % 4] = a.soft_pair(s_hi[1], e, l1);
-          if (g == 2) nw[0][e / 4][e % 4] = a.soft_pair(n_lo[0], e, l0);
-          if (g == 3) nw[1][e / 4][e % 4] = a.soft_pair(n_lo[1], e, l1);
-        }
-        if (g == 2 && i < A::NDMA) dma16(rk, lk + i * 1024, a.voff_k[i]);
-        if (g == 3 && i < A::NDMA) dma16(rv, lv + i * 1024, a.voff_v[i]);
+        if (g == 2 && i < A::NDMA) dma16(rk, a.dma_lds(ktile, i), a.voff_k[i]);
+        if (g == 3 && i < A::NDMA) dma16(rv, a.dma_lds(vtile, i), a.voff_v[i]);
         __builtin_amdgcn_sched_barrier(0);
       }
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        s_hi[qb] = n_hi[qb];
-#pragma unroll
-        for (int kc = 0; kc < 2; ++kc)
-#pragma unroll
-          for (int w = 0; w < 4; ++w) pw[qb][kc][w] = nw[qb][kc][w];
-      }
-    }
-    // Drain: PV of the last full tile (its V arrived with an earlier group).
+      sp.end_iteration(n_hi);
+    };
+    if (n_full > 1) iteration(0, std::true_type{});
+    for (int j = 1; j + 1 < n_full; ++j) iteration(j, std::false_type{});
+    // Drain: finish the pipeline, then PV of the last full tile (its V arrived
+    // with an earlier group).
+    if (n_full > 1) sp.flush();
     wait_vm<0>();
     __syncthreads();
     {
       const char* vt = a.vbuf((n_full - 1) % A::STAGES);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        pw[0][2 + e / 4][e % 4] = a.soft_pair(s_hi[0], e, l0);
-        pw[1][2 + e / 4][e % 4] = a.soft_pair(s_hi[1], e, l1);
-      }
+      float r0 = 0.f, r1 = 0.f;
+      a.soft(sp.s_hi[0], pb[0][2], pb[0][3], r0);
+      a.soft(sp.s_hi[1], pb[1][2], pb[1][3], r1);
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-        for (int kc = 0; kc < 4; ++kc) pb[qb][kc] = A::words(pw[qb][kc]);
+        for (int kc = 0; kc < 2; ++kc) pb[qb][kc] = A::words(sp.pw[qb][kc]);
       a.pv_half(vt, 0, pb);
       a.pv_half(vt, 1, pb);
+      l0 = sp.sum(0) + r0;
+      l1 = sp.sum(1) + r1;
     }
     a.l_run[0] = l0;
     a.l_run[1] = l1;
