@@ -30,6 +30,24 @@ PEAK_HBM_GBS = 8000.0
 POOL = 7                    # distinct input sets per pool (coprime to the layer count)
 
 
+TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "attn_bf16_kernel_480x480_traffic.json")
+ATTN_SOURCE = os.path.join(ROOT, "bounded_kv_cache_pr_amd", "csrc", "kernels_attn.hip")
+
+
+def measured_traffic():
+    """HBM bytes per attention launch from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE
+    record, or None when the kernel source has changed since it was taken."""
+    import hashlib
+    try:
+        with open(TRAFFIC_RECORD) as f:
+            rec = json.load(f)
+        with open(ATTN_SOURCE, "rb") as f:
+            sha = hashlib.sha256(f.read()).hexdigest()
+    except OSError:
+        return None
+    return rec["traffic_bytes_per_launch"] if rec.get("kernels_attn_hip_sha256") == sha else None
+
+
 def attn_flops(cfg) -> float:
     return 4.0 * cfg.n_heads * cfg.block_tokens * cfg.full_cache_keys * cfg.head_dim
 
@@ -164,7 +182,7 @@ def main():
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-            "traffic": None,
+            "traffic": measured_traffic(),
         },
     }
 
