@@ -88,6 +88,20 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t lds, ui
       : "memory");
 }
 
+// The same with a per-lane 64-bit global address (a gather).
+__device__ __forceinline__ void dma16_flat(const void* gaddr, uint32_t lds) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %2, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds), "v"(gaddr)
+      : "memory");
+}
+
 // s_waitcnt vmcnt(n), other counters untouched (gfx9 encoding).
 template <int N>
 __device__ __forceinline__ void wait_vm() {
@@ -159,8 +173,9 @@ struct Attn {
   static constexpr int UNITS = KT * NU;  // 16-byte units of one LDS tile
   static constexpr int NDMA = (UNITS + 255) / 256;  // DMA instructions per wave, tile and tensor
   static constexpr int TILE = KT * RBP;  // bytes per tile buffer
-  static constexpr int STAGES = 4;
-  static constexpr int LDS_BYTES = 2 * STAGES * TILE + 1024;  // K stages, V stages, DMA sink
+  static constexpr int STAGES = 3;
+  // K stages, V stages, the packed ragged K and V tile, DMA sink
+  static constexpr int LDS_BYTES = 2 * STAGES * TILE + 2 * TILE + 1024;
   static_assert(UNITS % 64 == 0, "a DMA instruction never straddles the end of a tile");
   static constexpr int NC = D / 16;      // QK^T k-steps
   static constexpr int NDB = D / 32;     // dv blocks
@@ -197,13 +212,56 @@ struct Attn {
 
   __device__ char* kbuf(int st) const { return smem + st * TILE; }
   __device__ char* vbuf(int st) const { return smem + (STAGES + st) * TILE; }
+  __device__ char* pkbuf() const { return smem + 2 * STAGES * TILE; }
+  __device__ char* pvbuf() const { return smem + (2 * STAGES + 1) * TILE; }
 
   // LDS destination of this wave's DMA instruction i into `tile`.  The four
   // waves issue NDMA instructions each; an instruction that falls wholly past
   // the tile (all its lanes are padding and load zeros) goes to a 1 KB sink.
   __device__ __forceinline__ uint32_t dma_lds(const char* tile, int i) const {
     const int u0 = (wave * NDMA + i) * 64;
-    return u0 < UNITS ? lds_addr(tile) + u0 * 16 : lds_addr(smem + 2 * STAGES * TILE);
+    return u0 < UNITS ? lds_addr(tile) + u0 * 16 : lds_addr(smem + (2 * STAGES + 2) * TILE);
+  }
+
+  // ---- packed ragged keys --------------------------------------------------
+  // The last count % 64 keys of every segment, concatenated in segment order
+  // (R of them), form packed tiles of 64 keys; with the keys already rotated,
+  // attention does not care which segment a key came from.  Packed key kk of
+  // this head: its K (or V) row.
+  __device__ const char* packed_row(int kk, bool k) const {
+    int off = 0;
+    const char* row = nullptr;
+    for (int s = 0; s < p.n_seg; ++s) {
+      const int cnt = p.seg[s].count, r = cnt % KT;
+      if (row == nullptr && kk < off + r) {
+        const char* base = static_cast<const char*>(k ? p.seg[s].k : p.seg[s].v);
+        row = base + (size_t)head * D * 2 + (size_t)(cnt - r + kk - off) * tok_bytes;
+      }
+      off += r;
+    }
+    return row;
+  }
+  __device__ int ragged_keys() const {
+    int r = 0;
+    for (int s = 0; s < p.n_seg; ++s) r += p.seg[s].count % KT;
+    return r;
+  }
+
+  // This wave's share of packed tile pt into kdst / vdst: a gather, one
+  // 16-byte global load per lane (rows past R repeat packed key 0 and are
+  // masked later; row padding loads the row's first 16 bytes, never read).
+  __device__ __forceinline__ void dma_packed(int pt, int R, char* kdst, char* vdst) const {
+#pragma unroll
+    for (int i = 0; i < NDMA; ++i) {
+      const int u = (wave * NDMA + i) * 64 + lane;
+      const int r = u / NU, c = u - r * NU;
+      const int cb = c < NS ? c * 16 : 0;
+      int kk = KT * pt + key_perm(r < KT ? r : 0), kv = KT * pt + (r < KT ? r : 0);
+      if (kk >= R) kk = 0;
+      if (kv >= R) kv = 0;
+      dma16_flat(packed_row(kk, true) + cb, dma_lds(kdst, i));
+      dma16_flat(packed_row(kv, false) + cb, dma_lds(vdst, i));
+    }
   }
 
   // Q' = bf16(rot(q) * log2(e)/sqrt(d)) as the QK^T B operand.
@@ -548,14 +606,14 @@ void attn_bf16_kernel(const AttnParams p) {
 
   int n_full = 0;
   for (int s = 0; s < p.n_seg; ++s) n_full += p.seg[s].count / A::KT;
+  const int n_ragged = a.ragged_keys();
 
   bool bad = false;
   if (n_full > 0) {
-    // K and V of tile t go to stage t % 4.  DMA groups: K0 alone, then
-    // {K1, V0}, {K2, V1}, {K3, V2}; iteration j issues {K(j+4), V(j+3)} after
-    // its barrier, which waits for every group but the newest (two iterations
-    // of latency).  Tiles past the last one load as zeros into stages nobody
-    // reads.
+    // K and V of tile t go to stage t % 3.  DMA groups: K0 alone, then
+    // {K1, V0}, {K2, V1}, the gather of the first packed ragged tile; iteration
+    // j issues {K(j+3), V(j+2)} after its barrier, which waits for every earlier
+    // group.  Tiles past the last one load as zeros into stages nobody reads.
     const size_t head_off = (size_t)head * D * 2;
     const uint32_t tile_bytes = A::KT * a.tok_bytes;
     TileCursor ck, cv;  // next K tile to load, next V tile to load
@@ -578,9 +636,12 @@ void attn_bf16_kernel(const AttnParams p) {
     load_v();  // V0
     load_k();  // K2
     load_v();  // V1
-    load_k();  // K3
-    load_v();  // V2
-    wait_vm<4 * A::NDMA>();  // K0, K1 and V0 landed
+    if (n_ragged > 0) {
+      a.dma_packed(0, n_ragged, a.pkbuf(), a.pvbuf());
+      wait_vm<4 * A::NDMA>();  // K0, K1 and V0 landed
+    } else {
+      wait_vm<2 * A::NDMA>();
+    }
     __syncthreads();
 
     // First tile, exact: sets each row's reference max m.
@@ -613,9 +674,9 @@ void attn_bf16_kernel(const AttnParams p) {
     // 0..31 of tile j), s_hi (scores of keys 32..63 of tile j, shifted by -m)
     // and the first three K operands of tile j+1 are ready.  The one barrier of
     // an iteration sits between groups B and C: it waits for the DMA group
-    // issued two iterations earlier ({K(j+2), V(j+1)}), so the next tile's first
+    // issued an iteration earlier ({K(j+2), V(j+1)}), so the next tile's first
     // operands can be read before the iteration ends; then the group
-    // {K(j+4), V(j+3)} is issued, one DMA per step of groups C and D.
+    // {K(j+3), V(j+2)} is issued, one DMA per step of groups C and D.
     //
     // Softmax runs as a five-stage software pipeline over the 32 packed pairs
     // of an iteration (pairs 0..7: s_hi of query block 0, 8..15: s_hi of block
@@ -653,7 +714,7 @@ void attn_bf16_kernel(const AttnParams p) {
       for (int t = 0; t < A::NOPS; ++t) {
         const int g = t / A::GA, i = t % A::GA;
         if (t == 2 * A::GA) {  // between groups B and C
-          wait_vm<2 * A::NDMA>();
+          wait_vm<0>();
           __syncthreads();
           rk = a.full_rsrc(ck.k, kt_next < n_full);
           rv = a.full_rsrc(cv.v, vt_next < n_full);
@@ -721,21 +782,33 @@ void attn_bf16_kernel(const AttnParams p) {
     a.init_queries(qt);
   }
 
-  // Exact, single-buffered passes: the ragged tiles, or every tile again after
-  // an overflow.
-  if (bad) a.reset_accumulators();
-  for (int s = 0; s < p.n_seg; ++s) {
-    const int cnt = p.seg[s].count;
-    for (int n0 = bad ? 0 : cnt - cnt % A::KT; n0 < cnt; n0 += A::KT) {
-      __amdgpu_buffer_rsrc_t rk, rv;
-      a.rsrc(s, n0, true, rk, rv);
-      a.dma_k(a.kbuf(0), rk);
-      a.dma_v(a.vbuf(0), rv);
+  // Exact, single-buffered passes: the packed ragged tiles (the first one is
+  // already in LDS when the pipelined loop ran), and after an overflow every
+  // full tile again.
+  if (bad) {
+    a.reset_accumulators();
+    for (int s = 0; s < p.n_seg; ++s) {
+      const int cnt = p.seg[s].count;
+      for (int n0 = 0; n0 + A::KT <= cnt; n0 += A::KT) {
+        __amdgpu_buffer_rsrc_t rk, rv;
+        a.rsrc(s, n0, true, rk, rv);
+        a.dma_k(a.kbuf(0), rk);
+        a.dma_v(a.vbuf(0), rv);
+        wait_vm<0>();
+        __syncthreads();
+        a.step_exact(a.kbuf(0), a.vbuf(0), n0, cnt);
+        __syncthreads();
+      }
+    }
+  }
+  for (int pt = 0; pt * A::KT < n_ragged; ++pt) {
+    if (pt > 0 || n_full == 0) {
+      a.dma_packed(pt, n_ragged, a.pkbuf(), a.pvbuf());
       wait_vm<0>();
       __syncthreads();
-      a.step_exact(a.kbuf(0), a.vbuf(0), n0, cnt);
-      __syncthreads();
     }
+    a.step_exact(a.pkbuf(), a.pvbuf(), pt * A::KT, n_ragged);
+    __syncthreads();
   }
   a.epilogue(qt);
 }
