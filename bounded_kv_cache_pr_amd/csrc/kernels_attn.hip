@@ -88,6 +88,42 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t lds, ui
       : "memory");
 }
 
+// The same inside a run of DMAs: M0 is saved by the run's first DMA
+// (dma16_save) and restored by its last (dma16_restore); nothing between them
+// reads M0.
+__device__ __forceinline__ uint32_t dma16_save(__amdgpu_buffer_rsrc_t r, uint32_t lds, uint32_t voff) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %2, %3, 0 offen lds"
+      : "=&s"(saved)
+      : "s"(lds), "v"(voff), "s"(r)
+      : "memory");
+  return saved;
+}
+__device__ __forceinline__ void dma16_mid(__amdgpu_buffer_rsrc_t r, uint32_t lds, uint32_t voff) {
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %1, %2, 0 offen lds"
+      :
+      : "s"(lds), "v"(voff), "s"(r)
+      : "memory");
+}
+__device__ __forceinline__ void dma16_restore(__amdgpu_buffer_rsrc_t r, uint32_t lds, uint32_t voff,
+                                              uint32_t saved) {
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %1, %2, 0 offen lds\n\t"
+      "s_mov_b32 m0, %3"
+      :
+      : "s"(lds), "v"(voff), "s"(r), "s"(saved)
+      : "memory");
+}
+
 // The same with a per-lane 64-bit global address (a gather).
 __device__ __forceinline__ void dma16_flat(const void* gaddr, uint32_t lds) {
   uint32_t saved;
@@ -710,6 +746,7 @@ void attn_bf16_kernel(const AttnParams p) {
       __amdgpu_buffer_rsrc_t rk, rv;
       const char* ktile = nullptr;
       const char* vtile = nullptr;
+      uint32_t m0_saved = 0;
 #pragma unroll
       for (int t = 0; t < A::NOPS; ++t) {
         const int g = t / A::GA, i = t % A::GA;
@@ -744,8 +781,14 @@ void attn_bf16_kernel(const AttnParams p) {
             a.o[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x, A::words(sp.pw[qb][kc]), a.o[qb][db], 0, 0, 0);
           }
         }
-        if (g == 2 && i < A::NDMA) dma16(rk, a.dma_lds(ktile, i), a.voff_k[i]);
-        if (g == 3 && i < A::NDMA) dma16(rv, a.dma_lds(vtile, i), a.voff_v[i]);
+        if ((g == 2 || g == 3) && i < A::NDMA) {
+          const __amdgpu_buffer_rsrc_t rr = g == 2 ? rk : rv;
+          const uint32_t la = a.dma_lds(g == 2 ? ktile : vtile, i);
+          const uint32_t vo = g == 2 ? a.voff_k[i] : a.voff_v[i];
+          if (g == 2 && i == 0) m0_saved = dma16_save(rr, la, vo);
+          else if (g == 3 && i == A::NDMA - 1) dma16_restore(rr, la, vo, m0_saved);
+          else dma16_mid(rr, la, vo);
+        }
         __builtin_amdgcn_sched_barrier(0);
       }
       sp.end_iteration(n_hi);
