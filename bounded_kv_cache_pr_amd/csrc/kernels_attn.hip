@@ -72,56 +72,53 @@ __device__ inline uint32_t lds_addr(const char* p) {
 }
 
 // 16 bytes per lane from a buffer resource into LDS: lane i writes
-// M0 + 16 i.  The load is invisible to the compiler's counters; callers wait
-// on vmcnt themselves.  M0 is saved and restored around it, and the LDS DMA
-// issues one wait state after the M0 write (the gfx9 M0 -> LDS-DMA hazard).
-__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t lds, uint32_t voff) {
+// M0 + 16 i; the global offset is voff + soff.  The load is invisible to the
+// compiler's counters; callers wait on vmcnt themselves.  M0 is saved and
+// restored around it, and the LDS DMA issues one wait state after the M0
+// write (the gfx9 M0 -> LDS-DMA hazard).
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t lds, uint32_t voff,
+                                      uint32_t soff = 0) {
   uint32_t saved;
   asm volatile(
       "s_mov_b32 %0, m0\n\t"
       "s_mov_b32 m0, %1\n\t"
       "s_nop 0\n\t"
-      "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
+      "buffer_load_dwordx4 %2, %3, %4 offen lds\n\t"
       "s_mov_b32 m0, %0"
       : "=&s"(saved)
-      : "s"(lds), "v"(voff), "s"(r)
+      : "s"(lds), "v"(voff), "s"(r), "s"(soff)
       : "memory");
 }
 
-// The same inside a run of DMAs: M0 is saved by the run's first DMA
-// (dma16_save) and restored by its last (dma16_restore); nothing between them
-// reads M0.
-__device__ __forceinline__ uint32_t dma16_save(__amdgpu_buffer_rsrc_t r, uint32_t lds, uint32_t voff) {
-  uint32_t saved;
+// The same inside a run of DMAs, with M0 = base + OFF set by one scalar add.
+// The run's first DMA (save) keeps M0 in `saved`, its last (restore) puts it
+// back; nothing between them reads M0.
+template <int OFF>
+__device__ __forceinline__ void dma16_imm(__amdgpu_buffer_rsrc_t r, uint32_t base, uint32_t voff,
+                                          uint32_t soff) {
   asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %1\n\t"
+      "s_add_u32 m0, %0, %4\n\t"
       "s_nop 0\n\t"
-      "buffer_load_dwordx4 %2, %3, 0 offen lds"
-      : "=&s"(saved)
-      : "s"(lds), "v"(voff), "s"(r)
-      : "memory");
-  return saved;
-}
-__device__ __forceinline__ void dma16_mid(__amdgpu_buffer_rsrc_t r, uint32_t lds, uint32_t voff) {
-  asm volatile(
-      "s_mov_b32 m0, %0\n\t"
-      "s_nop 0\n\t"
-      "buffer_load_dwordx4 %1, %2, 0 offen lds"
+      "buffer_load_dwordx4 %1, %2, %3 offen lds"
       :
-      : "s"(lds), "v"(voff), "s"(r)
-      : "memory");
+      : "s"(base), "v"(voff), "s"(r), "s"(soff), "i"(OFF)
+      : "memory", "scc");
 }
-__device__ __forceinline__ void dma16_restore(__amdgpu_buffer_rsrc_t r, uint32_t lds, uint32_t voff,
-                                              uint32_t saved) {
-  asm volatile(
-      "s_mov_b32 m0, %0\n\t"
-      "s_nop 0\n\t"
-      "buffer_load_dwordx4 %1, %2, 0 offen lds\n\t"
-      "s_mov_b32 m0, %3"
-      :
-      : "s"(lds), "v"(voff), "s"(r), "s"(saved)
-      : "memory");
+// k selects OFF = 4096 k (k is a constant once the caller's loop is unrolled).
+__device__ __forceinline__ void dma16_run(__amdgpu_buffer_rsrc_t r, uint32_t base, int k, uint32_t voff,
+                                          uint32_t soff, bool save, bool restore, uint32_t& saved) {
+  if (save) asm volatile("s_mov_b32 %0, m0" : "=s"(saved));
+  switch (k) {
+    case 0: dma16_imm<0>(r, base, voff, soff); break;
+    case 1: dma16_imm<4096>(r, base, voff, soff); break;
+    case 2: dma16_imm<8192>(r, base, voff, soff); break;
+    case 3: dma16_imm<12288>(r, base, voff, soff); break;
+    case 4: dma16_imm<16384>(r, base, voff, soff); break;
+    case 5: dma16_imm<20480>(r, base, voff, soff); break;
+    case 6: dma16_imm<24576>(r, base, voff, soff); break;
+    default: dma16_imm<28672>(r, base, voff, soff); break;
+  }
+  if (restore) asm volatile("s_mov_b32 m0, %0" : : "s"(saved));
 }
 
 // The same with a per-lane 64-bit global address (a gather).
@@ -162,34 +159,45 @@ __device__ __forceinline__ void mfma_qk_acc(f32x16& d, bf16x8 a, bf16x8 b) {
   asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "a"(b));
 }
 
-// Walks the full 64-key tiles of one head in segment order: k / v point at
-// the next tile's first key, `left` counts the full tiles still to come in the
-// current segment.  Moving to the next segment (the only scalar loads) happens
-// a handful of times per workgroup.
-struct TileCursor {
-  const char* k;
-  const char* v;
+// Walks the full 64-key tiles of one head, for K or V, in segment order: a
+// buffer resource per segment whose range is this head's rows of the segment,
+// and the byte offset of the next tile in it (the DMA's scalar offset).
+// Moving to the next segment (the only scalar loads) happens a handful of
+// times per workgroup.  Past the last tile the cursor stays on it, so loads
+// issued beyond the end re-read real data into stages nobody reads.
+struct SegCursor {
+  __amdgpu_buffer_rsrc_t r;
+  uint32_t off, step;
   int left, s;
-  __device__ __forceinline__ void seek(const AttnParams& p, size_t head_off) {
+  __device__ __forceinline__ void seek(const AttnParams& p, size_t head_off, uint32_t tok_bytes,
+                                       uint32_t tile_bytes, bool is_k) {
     while (s < p.n_seg && p.seg[s].count < kKeyTile) ++s;
     if (s < p.n_seg) {
-      k = static_cast<const char*>(p.seg[s].k) + head_off;
-      v = static_cast<const char*>(p.seg[s].v) + head_off;
+      const char* base = static_cast<const char*>(is_k ? p.seg[s].k : p.seg[s].v) + head_off;
+      const int nrec = (int)((size_t)p.seg[s].count * tok_bytes - head_off);
+      r = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), 0, nrec, 0x00020000);
+      off = 0;
+      step = tile_bytes;
       left = p.seg[s].count / kKeyTile;
+    } else {  // past the last tile: back onto it, and stay
+      off -= step;
+      step = 0;
+      left = 1 << 30;
     }
   }
-  __device__ __forceinline__ void first(const AttnParams& p, size_t head_off) {
+  // The first tile; the caller guarantees at least one full tile.
+  __device__ __forceinline__ void first(const AttnParams& p, size_t head_off, uint32_t tok_bytes,
+                                        uint32_t tile_bytes, bool is_k) {
     s = 0;
-    k = v = static_cast<const char*>(p.seg[0].k);
-    left = 0;
-    seek(p, head_off);
+    off = step = 0;
+    seek(p, head_off, tok_bytes, tile_bytes, is_k);
   }
-  __device__ __forceinline__ void next(const AttnParams& p, size_t head_off, uint32_t tile_bytes) {
-    k += tile_bytes;
-    v += tile_bytes;
+  __device__ __forceinline__ void next(const AttnParams& p, size_t head_off, uint32_t tok_bytes,
+                                       uint32_t tile_bytes, bool is_k) {
+    off += step;
     if (__builtin_expect(--left == 0, 0)) {
       ++s;
-      seek(p, head_off);
+      seek(p, head_off, tok_bytes, tile_bytes, is_k);
     }
   }
 };
@@ -208,11 +216,14 @@ struct Attn {
   static constexpr int NU = RBP / 16;    // 16-byte units per padded row
   static constexpr int UNITS = KT * NU;  // 16-byte units of one LDS tile
   static constexpr int NDMA = (UNITS + 255) / 256;  // DMA instructions per wave, tile and tensor
+  static constexpr int NBLK = UNITS / 64;           // 64-unit blocks of a tile (one DMA each)
   static constexpr int TILE = KT * RBP;  // bytes per tile buffer
   static constexpr int STAGES = 3;
   // K stages, V stages, the packed ragged K and V tile, DMA sink
   static constexpr int LDS_BYTES = 2 * STAGES * TILE + 2 * TILE + 1024;
   static_assert(UNITS % 64 == 0, "a DMA instruction never straddles the end of a tile");
+  static_assert(4 * (NDMA - 1) >= NBLK - 4 && 4 * NDMA >= NBLK,
+                "every block is covered and only the last instruction of a wave can fall past the tile");
   static constexpr int NC = D / 16;      // QK^T k-steps
   static constexpr int NDB = D / 32;     // dv blocks
   static constexpr float SUM_LIMIT = 18446744073709551616.0f;  // 2^64
@@ -223,6 +234,7 @@ struct Attn {
   uint32_t tok_bytes;
 
   uint32_t voff_k[NDMA], voff_v[NDMA];
+  bool last_ok;  // this wave's last DMA instruction lands inside the tile
 
   bf16x8 qreg[2][NC];
   f32x16 o[2][NDB];
@@ -235,10 +247,13 @@ struct Attn {
     hh = lane >> 5;
     l32 = lane & 31;
     tok_bytes = (uint32_t)(p.n_heads * D * 2);
-    // DMA unit u = (wave * NDMA + i) * 64 + lane of a tile -> (row, 16-byte slot)
+    // DMA instruction i of a wave moves unit block 4i + wave of a tile (only a
+    // wave's last one can fall past the tile); unit u = 64 block + lane ->
+    // (row, 16-byte slot)
+    last_ok = 4 * (NDMA - 1) + wave < NBLK;
 #pragma unroll
     for (int i = 0; i < NDMA; ++i) {
-      const int u = (wave * NDMA + i) * 64 + lane;
+      const int u = (4 * i + wave) * 64 + lane;
       const int r = u / NU, c = u - r * NU;
       const bool data = r < KT && c < NS;
       voff_k[i] = data ? (uint32_t)key_perm(r) * tok_bytes + c * 16 : kOutOfRange;
@@ -255,9 +270,9 @@ struct Attn {
   // waves issue NDMA instructions each; an instruction that falls wholly past
   // the tile (all its lanes are padding and load zeros) goes to a 1 KB sink.
   __device__ __forceinline__ uint32_t dma_lds(const char* tile, int i) const {
-    const int u0 = (wave * NDMA + i) * 64;
-    return u0 < UNITS ? lds_addr(tile) + u0 * 16 : lds_addr(smem + (2 * STAGES + 2) * TILE);
+    return i < NDMA - 1 || last_ok ? lds_addr(tile) + (4 * i + wave) * 1024 : sink();
   }
+  __device__ __forceinline__ uint32_t sink() const { return lds_addr(smem + (2 * STAGES + 2) * TILE); }
 
   // ---- packed ragged keys --------------------------------------------------
   // The last count % 64 keys of every segment, concatenated in segment order
@@ -289,7 +304,7 @@ struct Attn {
   __device__ __forceinline__ void dma_packed(int pt, int R, char* kdst, char* vdst) const {
 #pragma unroll
     for (int i = 0; i < NDMA; ++i) {
-      const int u = (wave * NDMA + i) * 64 + lane;
+      const int u = (4 * i + wave) * 64 + lane;
       const int r = u / NU, c = u - r * NU;
       const int cb = c < NS ? c * 16 : 0;
       int kk = KT * pt + key_perm(r < KT ? r : 0), kv = KT * pt + (r < KT ? r : 0);
@@ -349,12 +364,6 @@ struct Attn {
                                            0, nrec, kBufferConfig);
     rv = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(static_cast<const char*>(sg.v) + off),
                                            0, nrec, kBufferConfig);
-  }
-
-  // Buffer resource of a full tile starting at `base` (valid) or an empty one.
-  __device__ __forceinline__ __amdgpu_buffer_rsrc_t full_rsrc(const char* base, bool valid) const {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), 0,
-                                             valid ? (int)(KT * tok_bytes) : 0, kBufferConfig);
   }
 
   // This wave's share (NDMA instructions) of a K or V tile into LDS.
@@ -469,8 +478,8 @@ struct Attn {
   // sequence of NOPS steps in four groups: A = QK^T keys 0..31 (NC steps),
   // B = PV keys 0..31 (2*NDB steps), C = QK^T keys 32..63, D = PV keys 32..63.
   // Each step issues the LDS read of the operand three steps ahead, its two
-  // MFMAs (one per query block), and PAIRS packed softmax pairs; steps are
-  // fenced, so this order is the issue order.
+  // MFMAs (one per query block) and PAIRS packed softmax pairs split between
+  // the two MFMA shadows; steps are fenced, so this order is the issue order.
   static constexpr int GA = NC, GB = 2 * NDB;
   static constexpr int NOPS = 2 * GA + 2 * GB;
   static constexpr int PAIRS = 8 / GA;  // softmax pairs per step (GA == GB)
@@ -577,8 +586,15 @@ struct SoftPipe {
 
   // Stages due at step t.  FIRST: no earlier iteration (skip wrapped stages).
   // FLUSH: only the wrapped stages (the step after the last iteration).
+  // Parts of a pair's work, so a step's work can be split between the
+  // shadows of its two MFMAs.
+  static constexpr int kExp0 = 1, kExp1 = 2, kPack = 4, kAdd0 = 8, kAdd1 = 16, kAll = 31;
+
+  // Stages due at step t, the parts in `parts` only.  FIRST: no earlier
+  // iteration (skip wrapped stages).  FLUSH: only the wrapped stages (the
+  // step after the last iteration).
   template <bool FIRST, bool FLUSH>
-  __device__ __forceinline__ void run(int t, const f32x16& n_lo0, const f32x16& n_lo1) {
+  __device__ __forceinline__ void run(int t, const f32x16& n_lo0, const f32x16& n_lo1, int parts = kAll) {
 #pragma unroll
     for (int k = NSTAGE - 1; k >= 0; --k) {
       const int s0 = t - k;
@@ -588,26 +604,35 @@ struct SoftPipe {
 #pragma unroll
       for (int pp = 0; pp < PAIRS; ++pp) {
         const int q = (wrapped ? s0 + NOPS : s0) * PAIRS + pp;
+        const int qb = (q / 8) & 1;
         if (k == 0) {
           const f32x16& sv = q < 8 ? s_hi[0] : q < 16 ? s_hi[1] : q < 24 ? n_lo0 : n_lo1;
-          e[sl][pp][0] = __builtin_amdgcn_exp2f(sv[2 * (q % 8)]);
-          e[sl][pp][1] = __builtin_amdgcn_exp2f(sv[2 * (q % 8) + 1]);
-          asm volatile("" : "+v"(e[sl][pp][0]), "+v"(e[sl][pp][1]));
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+            if (parts & (kExp0 << h)) {
+              e[sl][pp][h] = __builtin_amdgcn_exp2f(sv[2 * (q % 8) + h]);
+              asm volatile("" : "+v"(e[sl][pp][h]));
+            }
         } else {
-          uint32_t& w = word(q, wrapped);
-          w = pack_bf16(e[sl][pp][0], e[sl][pp][1]);
-          const int qb = (q / 8) & 1;
-          acc[qb][0] += e[sl][pp][0];
-          acc[qb][1] += e[sl][pp][1];
-          asm volatile("" : "+v"(w), "+v"(acc[qb][0]), "+v"(acc[qb][1]));
+          if (parts & kPack) {
+            uint32_t& w = word(q, wrapped);
+            w = pack_bf16(e[sl][pp][0], e[sl][pp][1]);
+            asm volatile("" : "+v"(w));
+          }
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+            if (parts & (kAdd0 << h)) {
+              acc[qb][h] += e[sl][pp][h];
+              asm volatile("" : "+v"(acc[qb][h]));
+            }
         }
       }
     }
   }
 
   template <bool FIRST>
-  __device__ __forceinline__ void step(int t, const f32x16& n_lo0, const f32x16& n_lo1) {
-    run<FIRST, false>(t, n_lo0, n_lo1);
+  __device__ __forceinline__ void step(int t, int parts, const f32x16& n_lo0, const f32x16& n_lo1) {
+    run<FIRST, false>(t, n_lo0, n_lo1, parts);
   }
 
   // Closes an iteration: the new keys 32..63 become s_hi, and the words made
@@ -651,27 +676,24 @@ void attn_bf16_kernel(const AttnParams p) {
     // j issues {K(j+3), V(j+2)} after its barrier, which waits for every earlier
     // group.  Tiles past the last one load as zeros into stages nobody reads.
     const size_t head_off = (size_t)head * D * 2;
-    const uint32_t tile_bytes = A::KT * a.tok_bytes;
-    TileCursor ck, cv;  // next K tile to load, next V tile to load
-    ck.first(p, head_off);
-    cv = ck;
-    int kt_next = 0, vt_next = 0;
-    auto load_k = [&]() {
-      a.dma_k(a.kbuf(kt_next % A::STAGES), a.full_rsrc(ck.k, kt_next < n_full));
-      ++kt_next;
-      ck.next(p, head_off, tile_bytes);
+    const uint32_t tok_bytes = a.tok_bytes, tile_bytes = A::KT * tok_bytes;
+    SegCursor ck, cv;  // next K tile to load, next V tile to load
+    ck.first(p, head_off, tok_bytes, tile_bytes, true);
+    cv.first(p, head_off, tok_bytes, tile_bytes, false);
+    const uint32_t kbase = lds_addr(a.kbuf(0)), vbase = lds_addr(a.vbuf(0));
+    auto load = [&](SegCursor& c, uint32_t stage, const uint32_t (&voff)[A::NDMA], bool is_k) {
+#pragma unroll
+      for (int i = 0; i < A::NDMA; ++i)
+        dma16(c.r, i < A::NDMA - 1 || a.last_ok ? stage + (4 * i + a.wave) * 1024 : a.sink(), voff[i],
+              c.off);
+      c.next(p, head_off, tok_bytes, tile_bytes, is_k);
     };
-    auto load_v = [&]() {
-      a.dma_v(a.vbuf(vt_next % A::STAGES), a.full_rsrc(cv.v, vt_next < n_full));
-      ++vt_next;
-      cv.next(p, head_off, tile_bytes);
-    };
-    load_k();  // K0
+    load(ck, kbase, a.voff_k, true);  // K0
     a.init_queries(qt);
-    load_k();  // K1
-    load_v();  // V0
-    load_k();  // K2
-    load_v();  // V1
+    load(ck, kbase + A::TILE, a.voff_k, true);       // K1
+    load(cv, vbase, a.voff_v, false);                // V0
+    load(ck, kbase + 2 * A::TILE, a.voff_k, true);   // K2
+    load(cv, vbase + A::TILE, a.voff_v, false);      // V1
     if (n_ragged > 0) {
       a.dma_packed(0, n_ragged, a.pkbuf(), a.pvbuf());
       wait_vm<4 * A::NDMA>();  // K0, K1 and V0 landed
@@ -723,7 +745,8 @@ void attn_bf16_kernel(const AttnParams p) {
     // 3 unpack the rounded halves, 4 add them to the row sums.  The last
     // stages of an iteration's final pairs run in the next iteration's first
     // steps (or in the drain).
-    SoftPipe<A> sp;
+    using SP = SoftPipe<A>;
+    SP sp;
     sp.init(pb, l0, l1, s_hi);
     // queries live in AGPRs from here on (the QK^T MFMAs read them there)
 #pragma unroll
@@ -737,37 +760,45 @@ void attn_bf16_kernel(const AttnParams p) {
       ring[1] = a.op(A::NOPS + 1, kt, kt, kt);
       ring[2] = a.op(A::NOPS + 2, kt, kt, kt);
     }
-    auto iteration = [&](int j, auto first) {
+    // LDS byte offsets of stages j % 3, (j + 1) % 3 and (j + 2) % 3 in
+    // iteration j: QK^T reads K stage st1, PV reads V stage st0, the next
+    // tile's first operands come from K stage st2; K(j+3) goes to K stage st0
+    // and V(j+2) to V stage st2.
+    uint32_t st0 = 0, st1 = A::TILE, st2 = 2 * A::TILE;
+    const uint32_t wave_blk = a.wave * 1024;
+    auto iteration = [&](auto first) {
       constexpr bool FIRST = decltype(first)::value;
-      const char* kt = a.kbuf((j + 1) % A::STAGES);
-      const char* vt = a.vbuf(j % A::STAGES);
-      const char* kn = a.kbuf((j + 2) % A::STAGES);
+      const char* kt = a.kbuf(0) + st1;
+      const char* vt = a.vbuf(0) + st0;
+      const char* kn = a.kbuf(0) + st2;
       f32x16 n_lo[2], n_hi[2];
-      __amdgpu_buffer_rsrc_t rk, rv;
-      const char* ktile = nullptr;
-      const char* vtile = nullptr;
-      uint32_t m0_saved = 0;
+      uint32_t kdst = 0, vdst = 0, klast = 0, vlast = 0, m0_saved = 0;
 #pragma unroll
       for (int t = 0; t < A::NOPS; ++t) {
         const int g = t / A::GA, i = t % A::GA;
         if (t == 2 * A::GA) {  // between groups B and C
           wait_vm<0>();
           __syncthreads();
-          rk = a.full_rsrc(ck.k, kt_next < n_full);
-          rv = a.full_rsrc(cv.v, vt_next < n_full);
-          ktile = a.kbuf(kt_next % A::STAGES);
-          vtile = a.vbuf(vt_next % A::STAGES);
-          ++kt_next;
-          ++vt_next;
-          ck.next(p, head_off, tile_bytes);
-          cv.next(p, head_off, tile_bytes);
+          kdst = kbase + st0 + wave_blk;
+          vdst = vbase + st2 + wave_blk;
+          klast = a.last_ok ? kdst + (A::NDMA - 1) * 4096 : a.sink();
+          vlast = a.last_ok ? vdst + (A::NDMA - 1) * 4096 : a.sink();
           __builtin_amdgcn_sched_barrier(0);
         }
         ring[(t + 3) % 4] = a.op(t + 3, kt, vt, kn);
         const bf16x8 x = ring[t % 4];
-        sp.template step<FIRST>(t, n_lo[0], n_lo[1]);
+        // MFMA of query block 0 with the exponentials and the packing in its
+        // shadow, then MFMA of query block 1 with the row sums and the DMA in
+        // its shadow.  (An MFMA issued right behind another holds the wave
+        // until the first one drains, so work placed between two MFMAs is the
+        // only work that overlaps the first.)
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
+          if (qb == 1) {
+            __builtin_amdgcn_sched_barrier(0);
+            sp.template step<FIRST>(t, SP::kExp0 | SP::kExp1 | SP::kPack, n_lo[0], n_lo[1]);
+            __builtin_amdgcn_sched_barrier(0);
+          }
           if (g == 0) {
             if (i == 0) n_lo[qb] = mfma_qk_first(x, a.qreg[qb][i], cm[qb]);
             else mfma_qk_acc(n_lo[qb], x, a.qreg[qb][i]);
@@ -781,20 +812,29 @@ void attn_bf16_kernel(const AttnParams p) {
             a.o[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x, A::words(sp.pw[qb][kc]), a.o[qb][db], 0, 0, 0);
           }
         }
+        __builtin_amdgcn_sched_barrier(0);
+        sp.template step<FIRST>(t, SP::kAdd0 | SP::kAdd1, n_lo[0], n_lo[1]);
         if ((g == 2 || g == 3) && i < A::NDMA) {
-          const __amdgpu_buffer_rsrc_t rr = g == 2 ? rk : rv;
-          const uint32_t la = a.dma_lds(g == 2 ? ktile : vtile, i);
+          const SegCursor& c = g == 2 ? ck : cv;
           const uint32_t vo = g == 2 ? a.voff_k[i] : a.voff_v[i];
-          if (g == 2 && i == 0) m0_saved = dma16_save(rr, la, vo);
-          else if (g == 3 && i == A::NDMA - 1) dma16_restore(rr, la, vo, m0_saved);
-          else dma16_mid(rr, la, vo);
+          const bool save = t == 2 * A::GA, restore = t == 3 * A::GA + A::NDMA - 1;
+          if (i == A::NDMA - 1)
+            dma16_run(c.r, g == 2 ? klast : vlast, 0, vo, c.off, save, restore, m0_saved);
+          else
+            dma16_run(c.r, g == 2 ? kdst : vdst, i, vo, c.off, save, restore, m0_saved);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
+      ck.next(p, head_off, tok_bytes, tile_bytes, true);
+      cv.next(p, head_off, tok_bytes, tile_bytes, false);
       sp.end_iteration(n_hi);
+      const uint32_t t0 = st0;
+      st0 = st1;
+      st1 = st2;
+      st2 = t0;
     };
-    if (n_full > 1) iteration(0, std::true_type{});
-    for (int j = 1; j + 1 < n_full; ++j) iteration(j, std::false_type{});
+    if (n_full > 1) iteration(std::true_type{});
+    for (int j = 1; j + 1 < n_full; ++j) iteration(std::false_type{});
     // Drain: finish the pipeline, then PV of the last full tile (its V arrived
     // with an earlier group).
     if (n_full > 1) sp.flush();
