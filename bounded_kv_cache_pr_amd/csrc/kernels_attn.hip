@@ -56,15 +56,39 @@ __device__ inline uint32_t pack_bf16(float lo, float hi) {
 // Row r of a 64-row key tile lives at LDS row key_perm(r): bits 2 and 3 swapped.
 __device__ inline int key_perm(int r) { return (r & ~0xC) | ((r & 4) << 1) | ((r & 8) >> 1); }
 
-// XCD-aware tile order: consecutive workgroup ids land on different XCDs, so
-// every XCD gets whole heads; the query tiles of a head then share that XCD's
-// L2 while they stream the same keys.
-__device__ inline bool map_workgroup(const AttnParams& p, int& head, int& qt) {
+// XCD-aware work order: consecutive workgroup ids land on different XCDs
+// (xcd = id % 8), and XCD x takes the heads h = x (mod 8), so the query tiles
+// of a head share that XCD's L2 while they stream the same keys.  On each
+// XCD, job jx (head x + 8 (jx / n_qtiles), query tile jx % n_qtiles): the
+// first full_jobs run whole; the next tail_jobs run as `split` pieces each,
+// piece-major, so the pieces running side by side cover the same key range.
+struct Work {
+  int head, qt, piece, n_pieces, job;  // job: index among the XCD-major split jobs
+};
+__device__ inline bool map_work(const AttnParams& p, Work& w) {
   const int wg = blockIdx.x;
-  const int xcd = wg & 7, jx = wg >> 3;
-  head = xcd + 8 * (jx / p.n_qtiles);
-  qt = jx % p.n_qtiles;
-  return head < p.n_heads;
+  const int xcd = wg & 7, k = wg >> 3;
+  int jx;
+  if (k < p.full_jobs) {
+    jx = k;
+    w.piece = 0;
+    w.n_pieces = 1;
+    w.job = -1;
+  } else {
+    const int kk = k - p.full_jobs;
+    const int jt = kk % p.tail_jobs;
+    jx = p.full_jobs + jt;
+    w.piece = kk / p.tail_jobs;
+    w.n_pieces = p.split;
+    w.job = xcd * p.tail_jobs + jt;
+  }
+  // uniform per workgroup; the divisions above run on the VALU, so pin the
+  // results to SGPRs (buffer resources built from them must be scalar)
+  w.head = __builtin_amdgcn_readfirstlane(xcd + 8 * (jx / p.n_qtiles));
+  w.qt = __builtin_amdgcn_readfirstlane(jx % p.n_qtiles);
+  w.piece = __builtin_amdgcn_readfirstlane(w.piece);
+  w.job = __builtin_amdgcn_readfirstlane(w.job);
+  return w.head < p.n_heads;
 }
 
 __device__ inline uint32_t lds_addr(const char* p) {
@@ -185,12 +209,27 @@ struct SegCursor {
       left = 1 << 30;
     }
   }
-  // The first tile; the caller guarantees at least one full tile.
+  // Full tile `start` of the head (counting across segments); the caller
+  // guarantees it exists.
   __device__ __forceinline__ void first(const AttnParams& p, size_t head_off, uint32_t tok_bytes,
-                                        uint32_t tile_bytes, bool is_k) {
-    s = 0;
+                                        uint32_t tile_bytes, bool is_k, int start) {
+    // the segment holding tile `start`, by an unrolled scan of every slot
+    int acc = 0, sel = -1, skip = 0;
+#pragma unroll
+    for (int i = 0; i < kMaxSegments; ++i) {
+      const int n = p.seg[i].count / kKeyTile;
+      if (sel < 0 && start < acc + n) {
+        sel = i;
+        skip = start - acc;
+      }
+      acc += n;
+    }
+    s = __builtin_amdgcn_readfirstlane(sel);  // uniform: keep the resource in SGPRs
+    start = __builtin_amdgcn_readfirstlane(skip);
     off = step = 0;
     seek(p, head_off, tok_bytes, tile_bytes, is_k);
+    off = (uint32_t)start * tile_bytes;
+    left -= start;
   }
   __device__ __forceinline__ void next(const AttnParams& p, size_t head_off, uint32_t tok_bytes,
                                        uint32_t tile_bytes, bool is_k) {
@@ -280,21 +319,24 @@ struct Attn {
   // attention does not care which segment a key came from.  Packed key kk of
   // this head: its K (or V) row.
   __device__ const char* packed_row(int kk, bool k) const {
+    // unrolled over every segment slot (unused slots have count 0), with a
+    // select per slot: kk differs between lanes
     int off = 0;
     const char* row = nullptr;
-    for (int s = 0; s < p.n_seg; ++s) {
+#pragma unroll
+    for (int s = 0; s < kMaxSegments; ++s) {
       const int cnt = p.seg[s].count, r = cnt % KT;
-      if (row == nullptr && kk < off + r) {
-        const char* base = static_cast<const char*>(k ? p.seg[s].k : p.seg[s].v);
-        row = base + (size_t)head * D * 2 + (size_t)(cnt - r + kk - off) * tok_bytes;
-      }
+      const char* base = static_cast<const char*>(k ? p.seg[s].k : p.seg[s].v);
+      const char* cand = base + (size_t)head * D * 2 + (size_t)(cnt - r + kk - off) * tok_bytes;
+      row = kk >= off && kk < off + r ? cand : row;
       off += r;
     }
     return row;
   }
   __device__ int ragged_keys() const {
     int r = 0;
-    for (int s = 0; s < p.n_seg; ++s) r += p.seg[s].count % KT;
+#pragma unroll
+    for (int s = 0; s < kMaxSegments; ++s) r += p.seg[s].count % KT;
     return r;
   }
 
@@ -318,12 +360,13 @@ struct Attn {
   // Q' = bf16(rot(q) * log2(e)/sqrt(d)) as the QK^T B operand.
   __device__ void init_queries(int qt) {
     const float sc = p.scale_log2;
+    const RopeGeom g = p.g;  // in registers: the lookups below must not reload it
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
       const int qrow = qt * QT + wave * 64 + qb * 32 + l32;
       const bool valid = qrow < p.n_q;
       int tq = 0, yq = 0, xq = 0;
-      if (valid) token_pos(p.g, qrow, p.q_t_index, tq, yq, xq);
+      if (valid) token_pos(g, qrow, p.q_t_index, tq, yq, xq);
       const uint16_t* qp = static_cast<const uint16_t*>(p.q) + ((size_t)qrow * p.n_heads + head) * D;
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
@@ -332,7 +375,7 @@ struct Attn {
         uint32_t ws[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float2 cs = rope_cs(p.g, off / 2 + e, tq, yq, xq);
+          const float2 cs = rope_cs(g, off / 2 + e, tq, yq, xq);
           const float x0 = __uint_as_float(ws[e] << 16), x1 = __uint_as_float(ws[e] & 0xffff0000u);
           ws[e] = pack_bf16((x0 * cs.x - x1 * cs.y) * sc, (x0 * cs.y + x1 * cs.x) * sc);
         }
@@ -523,6 +566,73 @@ struct Attn {
     return __builtin_bit_cast(bf16x8, make_uint4(w[0], w[1], w[2], w[3]));
   }
 
+  // ---- split jobs ------------------------------------------------------
+  // A partial record holds this workgroup's unnormalised O (fp32, in the
+  // MFMA lane layout: float4 (dv 32db+8g+4hh .. +3) of query block qb at
+  // [((wave*2 + qb)*NDB + db)*4 + g][lane]) and (m, l) per lane at
+  // [(wave*2 + qb)][lane] after it; the workgroups that read a record run
+  // this same code, so the layout is the registers' own.  Records move with
+  // system-coherent buffer accesses (sc0 sc1): they bypass the XCD's L2, so
+  // handing one over needs no L2-wide write-back or invalidate, which would
+  // evict the keys the other workgroups of the XCD are sharing.
+  static constexpr int kCoherent = 1 | 16;  // sc0 | sc1
+  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+  typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+  static __device__ __forceinline__ __amdgpu_buffer_rsrc_t record(float* rec) {
+    return __builtin_amdgcn_make_buffer_rsrc(rec, 0, (int)(partial_record_floats(D) * 4), kBufferConfig);
+  }
+  __device__ void store_partial(float* rec) const {
+    const __amdgpu_buffer_rsrc_t r = record(rec);
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const u32x4 v = {__float_as_uint(o[qb][db][4 * g]), __float_as_uint(o[qb][db][4 * g + 1]),
+                           __float_as_uint(o[qb][db][4 * g + 2]), __float_as_uint(o[qb][db][4 * g + 3])};
+          __builtin_amdgcn_raw_buffer_store_b128(v, r, ((((wave * 2 + qb) * NDB + db) * 4 + g) * 64 + lane) * 16,
+                                                 0, kCoherent);
+        }
+      const u32x2 ml = {__float_as_uint(m_run[qb]), __float_as_uint(l_run[qb])};
+      __builtin_amdgcn_raw_buffer_store_b64(ml, r, 256 * D * 4 + ((wave * 2 + qb) * 64 + lane) * 8, 0, kCoherent);
+    }
+  }
+  // Folds another piece of the same job into the registers: both sides are
+  // rescaled to the larger reference max.  All of the record's loads are
+  // issued before any is used (coherent loads are not reordered, so waiting
+  // on each in turn would pay the memory latency once per load).
+  __device__ void merge_partial(float* rec) {
+    const __amdgpu_buffer_rsrc_t r = record(rec);
+    u32x2 ml[2];
+    u32x4 v[2][NDB][4];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      ml[qb] = __builtin_amdgcn_raw_buffer_load_b64(r, 256 * D * 4 + ((wave * 2 + qb) * 64 + lane) * 8, 0, kCoherent);
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          v[qb][db][g] = __builtin_amdgcn_raw_buffer_load_b128(
+              r, ((((wave * 2 + qb) * NDB + db) * 4 + g) * 64 + lane) * 16, 0, kCoherent);
+    }
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      const float mq = __uint_as_float(ml[qb].x), lq = __uint_as_float(ml[qb].y);
+      const float mx = fmaxf(m_run[qb], mq);
+      const float al = __builtin_amdgcn_exp2f(m_run[qb] - mx), be = __builtin_amdgcn_exp2f(mq - mx);
+      m_run[qb] = mx;
+      l_run[qb] = l_run[qb] * al + lq * be;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            o[qb][db][4 * g + e] = o[qb][db][4 * g + e] * al + __uint_as_float(v[qb][db][g][e]) * be;
+    }
+  }
+
   __device__ void epilogue(int qt) {
     // register 4g+e of dv block db is dv = 32db + 8g + 4hh + e
 #pragma unroll
@@ -660,26 +770,35 @@ void attn_bf16_kernel(const AttnParams p) {
   using A = Attn<D>;
   __shared__ __align__(16) char smem[A::LDS_BYTES];
   __shared__ int bad_flag[4];
+  __shared__ int last_piece;
 
-  int head, qt;
-  if (!map_workgroup(p, head, qt)) return;
+  Work w;
+  if (!map_work(p, w)) return;
+  const int head = w.head, qt = w.qt;
   A a(p, smem, head);
 
-  int n_full = 0;
-  for (int s = 0; s < p.n_seg; ++s) n_full += p.seg[s].count / A::KT;
+  int n_tiles = 0;  // full tiles of the head (unused segment slots have count 0)
+#pragma unroll
+  for (int s = 0; s < kMaxSegments; ++s) n_tiles += p.seg[s].count / A::KT;
   const int n_ragged = a.ragged_keys();
+  // this piece's units [u0, u1): full tiles [f0, f0 + n_full), then packed
+  // ragged tiles [pk0, pk1)
+  const int u0 = p.units * w.piece / w.n_pieces, u1 = p.units * (w.piece + 1) / w.n_pieces;
+  const int f0 = min(u0, n_tiles), n_full = min(u1, n_tiles) - f0;
+  const int pk0 = max(u0, n_tiles) - n_tiles, pk1 = max(u1, n_tiles) - n_tiles;
 
   bool bad = false;
   if (n_full > 0) {
-    // K and V of tile t go to stage t % 3.  DMA groups: K0 alone, then
-    // {K1, V0}, {K2, V1}, the gather of the first packed ragged tile; iteration
-    // j issues {K(j+3), V(j+2)} after its barrier, which waits for every earlier
-    // group.  Tiles past the last one load as zeros into stages nobody reads.
+    // K and V of tile t go to stage t % 3.  The prologue issues K0, K1, V0,
+    // K2, V1 and the gather of the first packed ragged tile, then rotates the
+    // queries while they land; iteration j issues {K(j+3), V(j+2)} after its
+    // barrier, which waits for every earlier group.  Tiles past the piece's
+    // last one re-read real keys into stages nobody reads.
     const size_t head_off = (size_t)head * D * 2;
     const uint32_t tok_bytes = a.tok_bytes, tile_bytes = A::KT * tok_bytes;
     SegCursor ck, cv;  // next K tile to load, next V tile to load
-    ck.first(p, head_off, tok_bytes, tile_bytes, true);
-    cv.first(p, head_off, tok_bytes, tile_bytes, false);
+    ck.first(p, head_off, tok_bytes, tile_bytes, true, f0);
+    cv.first(p, head_off, tok_bytes, tile_bytes, false, f0);
     const uint32_t kbase = lds_addr(a.kbuf(0)), vbase = lds_addr(a.vbuf(0));
     auto load = [&](SegCursor& c, uint32_t stage, const uint32_t (&voff)[A::NDMA], bool is_k) {
 #pragma unroll
@@ -688,18 +807,16 @@ void attn_bf16_kernel(const AttnParams p) {
               c.off);
       c.next(p, head_off, tok_bytes, tile_bytes, is_k);
     };
-    load(ck, kbase, a.voff_k, true);  // K0
-    a.init_queries(qt);
+    load(ck, kbase, a.voff_k, true);                 // K0
     load(ck, kbase + A::TILE, a.voff_k, true);       // K1
     load(cv, vbase, a.voff_v, false);                // V0
     load(ck, kbase + 2 * A::TILE, a.voff_k, true);   // K2
     load(cv, vbase + A::TILE, a.voff_v, false);      // V1
-    if (n_ragged > 0) {
-      a.dma_packed(0, n_ragged, a.pkbuf(), a.pvbuf());
-      wait_vm<4 * A::NDMA>();  // K0, K1 and V0 landed
-    } else {
-      wait_vm<2 * A::NDMA>();
-    }
+    if (pk1 > pk0) a.dma_packed(pk0, n_ragged, a.pkbuf(), a.pvbuf());
+    // the queries' loads and rotation overlap the DMAs; reading the loaded
+    // queries waits for every earlier load, so all groups have landed here
+    a.init_queries(qt);
+    wait_vm<0>();
     __syncthreads();
 
     // First tile, exact: sets each row's reference max m.
@@ -870,9 +987,10 @@ void attn_bf16_kernel(const AttnParams p) {
   // full tile again.
   if (bad) {
     a.reset_accumulators();
-    for (int s = 0; s < p.n_seg; ++s) {
+    for (int s = 0, t = 0; s < p.n_seg; ++s) {
       const int cnt = p.seg[s].count;
-      for (int n0 = 0; n0 + A::KT <= cnt; n0 += A::KT) {
+      for (int n0 = 0; n0 + A::KT <= cnt; n0 += A::KT, ++t) {
+        if (t < f0 || t >= f0 + n_full) continue;
         __amdgpu_buffer_rsrc_t rk, rv;
         a.rsrc(s, n0, true, rk, rv);
         a.dma_k(a.kbuf(0), rk);
@@ -884,14 +1002,34 @@ void attn_bf16_kernel(const AttnParams p) {
       }
     }
   }
-  for (int pt = 0; pt * A::KT < n_ragged; ++pt) {
-    if (pt > 0 || n_full == 0) {
+  for (int pt = pk0; pt < pk1; ++pt) {
+    if (pt > pk0 || n_full == 0) {
       a.dma_packed(pt, n_ragged, a.pkbuf(), a.pvbuf());
       wait_vm<0>();
       __syncthreads();
     }
     a.step_exact(a.pkbuf(), a.pvbuf(), pt * A::KT, n_ragged);
     __syncthreads();
+  }
+  if (w.n_pieces > 1) {
+    // Split job: publish this piece, and the last piece to arrive merges the
+    // others (the counter wraps back to 0 on that arrival).
+    const size_t rec = partial_record_floats(D);
+    float* const base = p.part + (size_t)w.job * w.n_pieces * rec;
+    // Ordering without cache-wide fences: every record access and the counter
+    // are system-coherent, each thread's stores have completed (vmcnt 0)
+    // before the barrier that precedes the counter update, and the other
+    // records are read only after the update has returned.
+    a.store_partial(base + (size_t)w.piece * rec);
+    wait_vm<0>();
+    __syncthreads();
+    if (threadIdx.x == 0)
+      last_piece = __builtin_amdgcn_atomic_inc32(p.cnt + w.job, (uint32_t)(w.n_pieces - 1), __ATOMIC_RELAXED,
+                                                 "") == (uint32_t)(w.n_pieces - 1);
+    __syncthreads();
+    if (!last_piece) return;
+    for (int r = 0; r < w.n_pieces; ++r)
+      if (r != w.piece) a.merge_partial(base + (size_t)r * rec);
   }
   a.epilogue(qt);
 }
@@ -967,13 +1105,56 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(const AttnParams p) {
   }
 }
 
+// Split plan of the bf16 kernel: per XCD, nj jobs on c CUs run as F = nj / c
+// rounds of whole jobs and R = nj % c jobs cut into s key ranges, s chosen
+// for the shortest estimated makespan.  A piece costs its share of a job plus
+// a start-up of about 8 key units and 15 % of a job: the chip runs power
+// limited, so a partly idle last round clocks higher and a split buys less
+// than the idle CUs suggest (measured at 480x480: 40 heads x 11 query tiles
+// on 256 CUs run fastest unsplit), while a handful of jobs on an otherwise
+// idle chip still gains from it.
+void plan_split(AttnParams& p, int n_cu) {
+  int c = n_cu / 8;
+  if (c < 1) c = 1;
+  if (c > kMaxCuPerXcd) c = kMaxCuPerXcd;
+  const int nj = (p.n_heads + 7) / 8 * p.n_qtiles;
+  const int F = nj / c, R = nj - F * c;
+  int best = 1;
+  if (R > 0 && p.part != nullptr) {
+    const double o = 0.15 + 8.0 / p.units;
+    double best_cost = 1e30;
+    for (int sp = 1; sp <= kMaxSplit && sp <= p.units; ++sp) {
+      const double cost = (double)((R * sp + c - 1) / c) * (1.0 / sp + o);
+      if (cost < best_cost - 1e-9) {
+        best_cost = cost;
+        best = sp;
+      }
+    }
+  }
+  if (best == 1) {  // every job whole
+    p.full_jobs = nj;
+    p.tail_jobs = 0;
+  } else {
+    p.full_jobs = F * c;
+    p.tail_jobs = R;
+  }
+  p.split = best;
+}
+
 }  // namespace
 
-hipError_t launch_attention(const AttnParams& p_in, int dtype, int head_dim, hipStream_t s) {
+hipError_t launch_attention(const AttnParams& p_in, int dtype, int head_dim, int n_cu, hipStream_t s) {
   AttnParams p = p_in;
   if (dtype == 0) {  // bf16
     p.n_qtiles = (p.n_q + 255) / 256;
-    const dim3 grid(8 * ((p.n_heads + 7) / 8) * p.n_qtiles);
+    int n_full = 0, n_rag = 0;
+    for (int i = 0; i < p.n_seg; ++i) {
+      n_full += p.seg[i].count / kKeyTile;
+      n_rag += p.seg[i].count % kKeyTile;
+    }
+    p.units = n_full + (n_rag + kKeyTile - 1) / kKeyTile;
+    plan_split(p, n_cu);
+    const dim3 grid(8 * (p.full_jobs + p.tail_jobs * p.split));
     if (head_dim == 128)
       hipLaunchKernelGGL(attn_bf16_kernel<128>, grid, dim3(256), 0, s, p);
     else

@@ -73,7 +73,9 @@ struct Layout {
   int elem, tpf, tb, tr, tb_pad, tr_pad;
   size_t kv_b, slot_b;   // block slot: one tensor of one layer, whole slot
   size_t kv_r, slot_r;   // Ref slot
-  size_t off_state, off_phi_bank, off_phi_cur, off_rope, off_cur_rot, off_ref, off_blocks, total;
+  size_t off_state, off_phi_bank, off_phi_cur, off_rope, off_cur_rot, off_part, off_cnt, off_ref, off_blocks,
+      total;
+  size_t n_part_rec, n_cnt;  // partial records and counters of split attention jobs
   int n_t, np_t, np_h, np_w, rope_h_off, rope_w_off, rope_entries;
   int n_block_slots;
 };
@@ -144,6 +146,15 @@ Layout make_layout(const pr_sink_config* c) {
   off = align_up(off + 8 * (size_t)L.rope_entries, kAlign);
   L.off_cur_rot = off;
   off = align_up(off + L.kv_b, kAlign);
+  // split attention jobs (bf16): per XCD fewer than kMaxCuPerXcd jobs are split,
+  // into at most kMaxSplit pieces, each piece one partial record
+  const bool split = c->dtype == PR_SINK_BF16;
+  L.n_cnt = split ? 8 * (size_t)kMaxCuPerXcd : 0;
+  L.n_part_rec = L.n_cnt * kMaxSplit;
+  L.off_part = off;
+  off = align_up(off + L.n_part_rec * partial_record_floats(c->head_dim) * sizeof(float), kAlign);
+  L.off_cnt = off;
+  off = align_up(off + L.n_cnt * sizeof(uint32_t), kAlign);
   L.off_ref = off;
   off += L.slot_r;
   L.off_blocks = off;
@@ -188,6 +199,7 @@ struct pr_sink_cache {
   int bank_count;     // entries filled so far (the first M blocks are inserted unconditionally)
   bool dyn_present;   // the open block attends the Dynamic Sink
   std::vector<uint8_t> ref_set, written;
+  int n_cu;           // compute units of the device
 
   char* block_slot(int bs) const { return arena + lay.off_blocks + (size_t)bs * lay.slot_b; }
   char* ref_slot() const { return arena + lay.off_ref; }
@@ -302,6 +314,7 @@ int pr_sink_cache_init(const pr_sink_config* cfg, void* arena_dev, size_t arena_
   if (!check_config(cfg)) return PR_SINK_EINVAL;
   const Layout L = make_layout(cfg);
   const bool dry = arena_dev == nullptr && arena_bytes == 0;
+  int n_cu = 0;
   if (!dry) {
     if (!arena_dev) return fail(PR_SINK_EINVAL, "arena is NULL");
     if (reinterpret_cast<uintptr_t>(arena_dev) & 255) return fail(PR_SINK_EINVAL, "arena must be 256-byte aligned");
@@ -313,6 +326,7 @@ int pr_sink_cache_init(const pr_sink_config* cfg, void* arena_dev, size_t arena_
     PRS_HIP(hipGetDeviceProperties(&prop, dev));
     if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0)
       return fail(PR_SINK_EHIP, "device %d is %s; this library is built for gfx950", dev, prop.gcnArchName);
+    n_cu = prop.multiProcessorCount;
     hipStream_t s = as_stream(stream);
     char* a = static_cast<char*>(arena_dev);
     PRS_HIP(hipMemsetAsync(a, 0, L.total, s));  // zero padding keeps masked keys finite
@@ -332,6 +346,7 @@ int pr_sink_cache_init(const pr_sink_config* cfg, void* arena_dev, size_t arena_
   c->open = false;
   c->bank_count = 0;
   c->dyn_present = false;
+  c->n_cu = n_cu;
   c->ref_set.assign(cfg->n_layers, 0);
   c->written.assign(cfg->n_layers, 0);
   *out = c;
@@ -460,7 +475,9 @@ int pr_sink_attend(pr_sink_cache* c, int32_t layer, const void* q_raw, const voi
   p.n_heads = g.n_heads;
   p.q_t_index = t_index[n_seg - 1];
   p.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)g.head_dim));
-  PRS_HIP(launch_attention(p, g.dtype, g.head_dim, st));
+  p.part = L.n_part_rec ? reinterpret_cast<float*>(c->arena + L.off_part) : nullptr;
+  p.cnt = L.n_cnt ? reinterpret_cast<uint32_t*>(c->arena + L.off_cnt) : nullptr;
+  PRS_HIP(launch_attention(p, g.dtype, g.head_dim, c->n_cu, st));
   return PR_SINK_OK;
 }
 

@@ -43,10 +43,16 @@ __device__ inline void token_pos(const RopeGeom& g, int n, int t_index, int& tt,
 
 // cos/sin of RoPE pair `pair` (adjacent elements 2*pair, 2*pair+1 of a head)
 // at position (tt, y, x): the t band covers the first np_t pairs, then h, then w.
+// The table index is chosen with selects, not branches: `pair` often differs
+// between lanes, and a branch per lookup would serialise the loads.
+__device__ inline int rope_index(const RopeGeom& g, int pair, int tt, int y, int x) {
+  const int it = tt * g.np_t + pair;
+  const int ih = g.rope_h_off + y * g.np_h + (pair - g.np_t);
+  const int iw = g.rope_w_off + x * g.np_w + (pair - g.np_t - g.np_h);
+  return pair < g.np_t ? it : pair < g.np_t + g.np_h ? ih : iw;
+}
 __device__ inline float2 rope_cs(const RopeGeom& g, int pair, int tt, int y, int x) {
-  if (pair < g.np_t) return g.rope[tt * g.np_t + pair];
-  if (pair < g.np_t + g.np_h) return g.rope[g.rope_h_off + y * g.np_h + pair - g.np_t];
-  return g.rope[g.rope_w_off + x * g.np_w + pair - g.np_t - g.np_h];
+  return g.rope[rope_index(g, pair, tt, y, x)];
 }
 
 // One attended segment of the cache as the attention kernel sees it.  K and V
@@ -71,7 +77,26 @@ struct AttnParams {
   int32_t q_t_index;    // temporal table row of the current block's first frame
   int32_t n_qtiles;
   float scale_log2;     // log2(e) / sqrt(d)
+  // Work split of the bf16 kernel.  A job is one (head, 256-query tile); its
+  // keys are `units` 64-key units (the full tiles, then the packed ragged
+  // tiles).  Each XCD takes the heads h = xcd (mod 8): its first `full_jobs`
+  // jobs run whole, the next `tail_jobs` are each cut into `split` key ranges
+  // whose partial results (`part`) are merged by the last piece to arrive
+  // (`cnt`, one self-resetting counter per split job).
+  int32_t full_jobs;
+  int32_t tail_jobs;
+  int32_t split;
+  int32_t units;
+  float* part;
+  uint32_t* cnt;
 };
+
+// Largest split of a job's keys the partial-record workspace is sized for, and
+// the most CUs per XCD the work split plans for.
+constexpr int kMaxSplit = 4;
+constexpr int kMaxCuPerXcd = 32;
+// Floats of one partial record: 256 rows x d of O, then (m, l) per lane.
+__host__ __device__ constexpr size_t partial_record_floats(int head_dim) { return 256 * (size_t)head_dim + 2 * 512; }
 
 // Bank / retrieval state kept in device memory inside the arena.
 struct DevState {
@@ -105,7 +130,8 @@ struct RotParams {
 };
 
 // Launchers (kernels_*.hip).  All return the launch status.
-hipError_t launch_attention(const AttnParams& p, int dtype, int head_dim, hipStream_t s);
+// n_cu: compute units of the device (sizes the work split of the bf16 kernel).
+hipError_t launch_attention(const AttnParams& p, int dtype, int head_dim, int n_cu, hipStream_t s);
 hipError_t launch_rope_follow(const RotParams& p, int n_layers, hipStream_t s);
 hipError_t launch_kv_write(const void* k_src, const void* v_src, void* k_dst0, void* v_dst0,
                            void* k_dst1, void* v_dst1, size_t bytes, hipStream_t s);

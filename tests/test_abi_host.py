@@ -46,6 +46,11 @@ def test_arena_bytes_closed_form():
         # block's rotated K
         kv = 3 * cfg.n_layers * row * (pad(cfg.ref_tokens) + slots * pad(cfg.block_tokens))
         kv += row * pad(cfg.block_tokens)
+        if cfg.dtype == synth.DTYPE_BF16:
+            # split attention jobs: up to 4 pieces of each of up to 32 jobs per
+            # XCD (8 XCDs), one fp32 partial record per piece (256 rows x d of
+            # O, plus (m, l) per lane), and one counter per split job
+            kv += 8 * 32 * 4 * (256 * cfg.head_dim + 1024) * 4 + 8 * 32 * 4
         n = binding.arena_bytes(cfg)
         slack = (slots + 3) * 4096 + 3 * cfg.n_layers * (slots + 1) * 256 + (1 << 20)
         assert kv <= n <= kv + slack
