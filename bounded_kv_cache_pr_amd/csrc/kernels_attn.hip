@@ -193,11 +193,12 @@ struct SegCursor {
   __amdgpu_buffer_rsrc_t r;
   uint32_t off, step;
   int left, s;
+  int dyn_r;  // bank entry of the Dynamic Sink (load_dyn_r)
   __device__ __forceinline__ void seek(const AttnParams& p, size_t head_off, uint32_t tok_bytes,
                                        uint32_t tile_bytes, bool is_k) {
     while (s < p.n_seg && p.seg[s].count < kKeyTile) ++s;
     if (s < p.n_seg) {
-      const char* base = static_cast<const char*>(is_k ? p.seg[s].k : p.seg[s].v) + head_off;
+      const char* base = seg_base(p, s, is_k, dyn_r) + head_off;
       const int nrec = (int)((size_t)p.seg[s].count * tok_bytes - head_off);
       r = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), 0, nrec, 0x00020000);
       off = 0;
@@ -212,7 +213,8 @@ struct SegCursor {
   // Full tile `start` of the head (counting across segments); the caller
   // guarantees it exists.
   __device__ __forceinline__ void first(const AttnParams& p, size_t head_off, uint32_t tok_bytes,
-                                        uint32_t tile_bytes, bool is_k, int start) {
+                                        uint32_t tile_bytes, bool is_k, int start, int dyn) {
+    dyn_r = dyn;
     // the segment holding tile `start`, by an unrolled scan of every slot
     int acc = 0, sel = -1, skip = 0;
 #pragma unroll
@@ -270,6 +272,7 @@ struct Attn {
   const AttnParams& p;
   char* smem;  // K stages then V stages
   int head, lane, wave, hh, l32;
+  int dyn_r;  // bank entry of the Dynamic Sink
   uint32_t tok_bytes;
 
   uint32_t voff_k[NDMA], voff_v[NDMA];
@@ -280,6 +283,7 @@ struct Attn {
   float m_run[2], l_run[2];
 
   __device__ Attn(const AttnParams& p_, char* smem_, int head_) : p(p_), smem(smem_), head(head_) {
+    dyn_r = load_dyn_r(p);
     const int tid = threadIdx.x;
     lane = tid & 63;
     wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -326,7 +330,7 @@ struct Attn {
 #pragma unroll
     for (int s = 0; s < kMaxSegments; ++s) {
       const int cnt = p.seg[s].count, r = cnt % KT;
-      const char* base = static_cast<const char*>(k ? p.seg[s].k : p.seg[s].v);
+      const char* base = seg_base(p, s, k, dyn_r);
       const char* cand = base + (size_t)head * D * 2 + (size_t)(cnt - r + kk - off) * tok_bytes;
       row = kk >= off && kk < off + r ? cand : row;
       off += r;
@@ -400,13 +404,14 @@ struct Attn {
   // segment is touched.  valid == false gives an empty range (all zeros).
   __device__ __forceinline__ void rsrc(int s, int n0, bool valid, __amdgpu_buffer_rsrc_t& rk,
                                        __amdgpu_buffer_rsrc_t& rv) const {
-    const Segment& sg = p.seg[valid ? s : 0];
+    const int si = valid ? s : 0;
+    const Segment& sg = p.seg[si];
     const size_t off = valid ? (size_t)head * sg.head * 2 + (size_t)n0 * tok_bytes : 0;
     const int nrec = valid ? (int)((size_t)(sg.count - n0) * tok_bytes) : 0;
-    rk = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(static_cast<const char*>(sg.k) + off),
-                                           0, nrec, kBufferConfig);
-    rv = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(static_cast<const char*>(sg.v) + off),
-                                           0, nrec, kBufferConfig);
+    rk = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(seg_base(p, si, true, dyn_r) + off), 0, nrec,
+                                           kBufferConfig);
+    rv = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(seg_base(p, si, false, dyn_r) + off), 0, nrec,
+                                           kBufferConfig);
   }
 
   // This wave's share (NDMA instructions) of a K or V tile into LDS.
@@ -797,8 +802,8 @@ void attn_bf16_kernel(const AttnParams p) {
     const size_t head_off = (size_t)head * D * 2;
     const uint32_t tok_bytes = a.tok_bytes, tile_bytes = A::KT * tok_bytes;
     SegCursor ck, cv;  // next K tile to load, next V tile to load
-    ck.first(p, head_off, tok_bytes, tile_bytes, true, f0);
-    cv.first(p, head_off, tok_bytes, tile_bytes, false, f0);
+    ck.first(p, head_off, tok_bytes, tile_bytes, true, f0, a.dyn_r);
+    cv.first(p, head_off, tok_bytes, tile_bytes, false, f0, a.dyn_r);
     const uint32_t kbase = lds_addr(a.kbuf(0)), vbase = lds_addr(a.vbuf(0));
     auto load = [&](SegCursor& c, uint32_t stage, const uint32_t (&voff)[A::NDMA], bool is_k) {
 #pragma unroll
@@ -1066,12 +1071,13 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(const AttnParams p) {
 #pragma unroll
   for (int i = 0; i < D; ++i) o[i] = 0.f;
   float m_run = -INFINITY, l_run = 0.f;
+  const int dyn_r = load_dyn_r(p);
 
   for (int s = 0; s < p.n_seg; ++s) {
     const Segment sg = p.seg[s];
     const int count = sg.count;
-    const float* kbase = static_cast<const float*>(sg.k) + (size_t)head * sg.head;
-    const float* vbase = static_cast<const float*>(sg.v) + (size_t)head * sg.head;
+    const float* kbase = reinterpret_cast<const float*>(seg_base(p, s, true, dyn_r)) + (size_t)head * sg.head;
+    const float* vbase = reinterpret_cast<const float*>(seg_base(p, s, false, dyn_r)) + (size_t)head * sg.head;
     for (int n0 = 0; n0 < count; n0 += KT) {
       for (int id = lane; id < KT * D; id += KT) {
         const int r = id / D, dv = id % D;

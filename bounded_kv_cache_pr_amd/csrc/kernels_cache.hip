@@ -143,8 +143,7 @@ __global__ __launch_bounds__(64) void retrieve_kernel(const float* __restrict__ 
                                                       double* __restrict__ phi_cur,
                                                       const double* __restrict__ bank_phi,
                                                       DevState* __restrict__ st, int fp_dim,
-                                                      int bank_count, int block, int dyn_slot,
-                                                      int bank_slot0, int32_t* slot_out) {
+                                                      int bank_count, int block, int32_t* slot_out) {
   const int lane = threadIdx.x;
   // phi_b = x / ||x||_2, zero stays zero
   double ss = 0.0;
@@ -166,17 +165,10 @@ __global__ __launch_bounds__(64) void retrieve_kernel(const float* __restrict__ 
     if (st->ids[s] == block - 1) continue;
     if (r < 0 || sc > best) { r = s; best = sc; }
   }
-  if (lane == 0) {
+  if (lane == 0) {  // the Dynamic Sink of this block is bank entry r (none if r < 0)
     st->last_r = r;
+    st->dyn_id = r >= 0 ? st->ids[r] : -1;
     if (slot_out) *slot_out = r;
-    if (r >= 0 && st->ids[r] != st->dyn_id) {
-      st->copy_src = bank_slot0 + r;
-      st->copy_dst = dyn_slot;
-      st->dyn_id = st->ids[r];
-    } else {
-      st->copy_src = -1;
-      if (r < 0) st->dyn_id = -1;
-    }
   }
 }
 
@@ -281,10 +273,10 @@ hipError_t launch_slot_copy(char* block_base, size_t slot_bytes, size_t copy_byt
 }
 
 hipError_t launch_retrieve(const float* fp_raw, double* phi_cur, const double* bank_phi,
-                           DevState* st, int fp_dim, int bank_count, int block, int dyn_slot,
-                           int bank_slot0, int32_t* slot_out, hipStream_t s) {
+                           DevState* st, int fp_dim, int bank_count, int block, int32_t* slot_out,
+                           hipStream_t s) {
   hipLaunchKernelGGL(retrieve_kernel, dim3(1), dim3(64), 0, s, fp_raw, phi_cur, bank_phi, st,
-                     fp_dim, bank_count, block, dyn_slot, bank_slot0, slot_out);
+                     fp_dim, bank_count, block, slot_out);
   return hipGetLastError();
 }
 

@@ -126,7 +126,9 @@ Layout make_layout(const pr_sink_config* c) {
   L.slot_b = align_up(3 * L.kv_b * c->n_layers, kAlign);
   L.kv_r = align_up(hd * L.tr_pad, 256);
   L.slot_r = align_up(3 * L.kv_r * c->n_layers, kAlign);
-  L.n_block_slots = 2 + c->window_slots + c->bank_size;
+  // Static, the window, the bank; the Dynamic Sink is a reference to a bank
+  // entry and takes no slot of its own
+  L.n_block_slots = 1 + c->window_slots + c->bank_size;
   // temporal positions: Ref, Static, Dynamic, W-1 previous blocks, current
   L.n_t = c->ref_frames + (c->window_slots + 2) * c->block_frames;
   L.np_t = c->rope_dims[0] / 2;
@@ -212,9 +214,8 @@ struct pr_sink_cache {
   double* phi_cur() const { return reinterpret_cast<double*>(arena + lay.off_phi_cur); }
   const float2* rope() const { return reinterpret_cast<const float2*>(arena + lay.off_rope); }
   int bs_static() const { return 0; }
-  int bs_dynamic() const { return 1; }
-  int bs_window(int j) const { return 2 + j; }
-  int bs_bank(int i) const { return 2 + cfg.window_slots + i; }
+  int bs_window(int j) const { return 1 + j; }
+  int bs_bank(int i) const { return 1 + cfg.window_slots + i; }
 };
 
 namespace {
@@ -392,10 +393,10 @@ int pr_sink_retrieve(pr_sink_cache* c, int32_t block, const float* fp_raw_dev,
     const pr_sink_config& g = c->cfg;
     const Layout& L = c->lay;
     hipStream_t s = as_stream(stream);
+    // r lands in the device state; attention reads bank entry r in place (its
+    // K is kept rotated at the Dynamic Sink's place), so nothing is copied
     PRS_HIP(launch_retrieve(fp_raw_dev, c->phi_cur(), c->phi_bank(), c->state(), g.fp_dim,
-                            c->bank_count, block, c->bs_dynamic(), c->bs_bank(0), slot_out_dev, s));
-    // Dynamic Sink <- bank entry r: raw K, V and K already rotated at the Dynamic place
-    PRS_HIP(launch_slot_copy(c->block_slot(0), L.slot_b, 3 * L.kv_b * g.n_layers, c->state(), s));
+                            c->bank_count, block, slot_out_dev, s));
     // RoPE follow for the blocks whose place changes as this block opens: every
     // previous window block moves one place, and block 0 becomes the Static Sink.
     RotParams r = rot_params(c, L.tb, L.kv_b);
@@ -441,6 +442,7 @@ int pr_sink_attend(pr_sink_cache* c, int32_t layer, const void* q_raw, const voi
     PRS_HIP(launch_rope_follow(r, 1, st));
   }
   AttnParams p{};
+  p.dyn_seg = -1;
   const int64_t D = g.head_dim;
   const int b = c->next_block;
   for (int s = 0; s < n_seg; ++s) {
@@ -455,10 +457,18 @@ int pr_sink_attend(pr_sink_cache* c, int32_t layer, const void* q_raw, const voi
     } else if (s == n_seg - 1) {  // current block: rotated copy, caller's V
       sg.k = cur_rot;
       sg.v = v_cur_raw;
+    } else if (s == 2) {  // Dynamic Sink: bank entry r, resolved on the device
+      sg.k = sg.v = nullptr;
+      if (tokens[s] > 0) {
+        p.dyn_seg = s;
+        p.dyn_r = &c->state()->last_r;
+        p.dyn_k0 = c->block_slot(c->bs_bank(0)) + c->r_off(layer, L.kv_b);
+        p.dyn_v0 = c->block_slot(c->bs_bank(0)) + c->v_off(layer, L.kv_b);
+        p.dyn_stride = (int64_t)L.slot_b;
+      }
     } else {
       int bs;
       if (s == 1) bs = c->bs_static();
-      else if (s == 2) bs = c->bs_dynamic();
       else {
         const int id = b - (g.window_slots - 1) + (s - 3);
         bs = c->bs_window(id >= 0 ? id % g.window_slots : 0);
@@ -558,8 +568,10 @@ int pr_sink_slot_view(const pr_sink_cache* c, int32_t slot, int32_t layer, void*
   if (!k_dev || !v_dev || !t_pad_out) return fail(PR_SINK_EINVAL, "NULL output pointer");
   if (c->dry) return fail(PR_SINK_EINVAL, "dry-run cache has no arena");
   const Layout& L = c->lay;
-  const int n_slots = 1 + L.n_block_slots;
+  const int n_slots = 2 + L.n_block_slots;  // Ref, the Dynamic id, the block slots
   if (slot < 0 || slot >= n_slots) return fail(PR_SINK_EINVAL, "slot %d out of range", slot);
+  if (slot == PR_SINK_SLOT_DYNAMIC)
+    return fail(PR_SINK_EINVAL, "the Dynamic Sink is bank entry r (pr_sink_retrieve's slot_out), not a slot of its own; view that bank entry");
   char* base;
   size_t kv;
   if (slot == PR_SINK_SLOT_REF) {
@@ -567,7 +579,7 @@ int pr_sink_slot_view(const pr_sink_cache* c, int32_t slot, int32_t layer, void*
     kv = L.kv_r;
     *t_pad_out = L.tr_pad;
   } else {
-    base = c->block_slot(slot - 1);
+    base = c->block_slot(slot == PR_SINK_SLOT_STATIC ? c->bs_static() : slot - PR_SINK_SLOT_WINDOW0 + 1);
     kv = L.kv_b;
     *t_pad_out = L.tb_pad;
   }

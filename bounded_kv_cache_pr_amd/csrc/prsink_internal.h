@@ -89,7 +89,36 @@ struct AttnParams {
   int32_t units;
   float* part;
   uint32_t* cnt;
+  // The Dynamic Sink is not a copy: segment dyn_seg (-1 = none) reads bank
+  // entry r = *dyn_r, whose rotated K (dyn_k0) and V (dyn_v0) sit dyn_stride
+  // bytes apart per entry.  r is read on the device, so the host never waits
+  // for the retrieval.
+  const int32_t* dyn_r;
+  const char* dyn_k0;
+  const char* dyn_v0;
+  int64_t dyn_stride;
+  int32_t dyn_seg;
 };
+
+// The bank entry the Dynamic Sink reads, loaded once per workgroup with a
+// scalar load (the value then stays in SGPRs, so addresses built from it can
+// feed buffer resources; the load waits for itself inside the asm).  0 when
+// the block has no Dynamic Sink or no entry was found.
+__device__ inline int load_dyn_r(const AttnParams& p) {
+  if (p.dyn_seg < 0) return 0;
+  int r;
+  asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(r) : "s"(p.dyn_r) : "memory");
+  return r > 0 ? r : 0;
+}
+
+// K (is_k) or V base of segment s; dyn_r from load_dyn_r.  Written as a
+// select of two computed bases: an early return here let the compiler treat
+// the result as divergent and move it to VGPRs.
+__device__ inline const char* seg_base(const AttnParams& p, int s, bool is_k, int dyn_r) {
+  const char* dyn = (is_k ? p.dyn_k0 : p.dyn_v0) + (int64_t)dyn_r * p.dyn_stride;
+  const char* seg = static_cast<const char*>(is_k ? p.seg[s].k : p.seg[s].v);
+  return s == p.dyn_seg ? dyn : seg;
+}
 
 // Largest split of a job's keys the partial-record workspace is sized for, and
 // the most CUs per XCD the work split plans for.
@@ -102,7 +131,7 @@ __host__ __device__ constexpr size_t partial_record_floats(int head_dim) { retur
 struct DevState {
   int32_t ids[kMaxBank];   // block id per bank entry, -1 = empty
   int32_t last_r;          // last retrieved bank entry, -1 = none
-  int32_t dyn_id;          // block id whose K/V sit in the Dynamic slot, -1 = none
+  int32_t dyn_id;          // block id of the open block's Dynamic Sink (bank entry last_r), -1 = none
   int32_t decision;        // last bank decision: -2 none, -1 keep, j = entry written
   int32_t copy_src;        // pending slot copy: source block-slot index, -1 = skip
   int32_t copy_dst;        // destination block-slot index
@@ -139,7 +168,7 @@ hipError_t launch_slot_copy(char* block_base, size_t slot_bytes, size_t copy_byt
                             const DevState* st, hipStream_t s);
 hipError_t launch_retrieve(const float* fp_raw, double* phi_cur, const double* bank_phi,
                            DevState* st, int fp_dim, int bank_count, int block,
-                           int dyn_slot, int bank_slot0, int32_t* slot_out, hipStream_t s);
+                           int32_t* slot_out, hipStream_t s);
 hipError_t launch_bank_update(const double* phi_cur, double* bank_phi, DevState* st,
                               int fp_dim, int bank_size, int bank_count, int block,
                               int win_slot, int bank_slot0, hipStream_t s);

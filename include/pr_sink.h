@@ -95,7 +95,10 @@ typedef struct pr_sink_config {
 
 typedef struct pr_sink_cache pr_sink_cache; /* opaque, host-side handle */
 
-/* Slot ids for pr_sink_slot_view. */
+/* Slot ids for pr_sink_slot_view.  PR_SINK_SLOT_DYNAMIC names the Dynamic
+ * Sink, which has no storage of its own (it reads the bank entry that
+ * pr_sink_retrieve returned); pr_sink_slot_view rejects it with
+ * PR_SINK_EINVAL. */
 enum {
   PR_SINK_SLOT_REF = 0,
   PR_SINK_SLOT_STATIC = 1,
@@ -127,11 +130,14 @@ int pr_sink_set_ref(pr_sink_cache* c, int32_t layer, const void* k_raw, const vo
  * fingerprint fp_raw_dev (device float[fp_dim]) to unit l2 norm in fp64 (an
  * all-zero fingerprint stays zero), scores it by dot product against every
  * bank entry whose block id is not block-1, takes the argmax (lowest slot on
- * ties) and copies that entry's K/V of all layers into the Dynamic Sink
- * (review, full-pipeline paragraph: r(b) = argmax phi_b . phi_i excluding b-1;
- * novelty paragraph: cosine similarity of l2-normalised fingerprints).  If no
- * entry is eligible the Dynamic Sink is not attended during this block.  The
- * copy is skipped when the entry's block already sits in the Dynamic Sink.
+ * ties), and makes that entry the block's Dynamic Sink (review, full-pipeline
+ * paragraph: r(b) = argmax phi_b . phi_i excluding b-1, whose K/V go to the
+ * Dynamic Sink; novelty paragraph: cosine similarity of l2-normalised
+ * fingerprints).  Nothing is copied: attention reads bank entry r in place,
+ * whose keys are kept rotated at the Dynamic Sink's place, and r stays on the
+ * device (the host never waits for the retrieval).  The entry cannot change
+ * while the block is open: the bank is written only by pr_sink_bank_update.
+ * If no entry is eligible the Dynamic Sink is not attended during this block.
  * Also re-rotates the keys of the blocks whose place changes as block opens.
  * slot_out_dev (device int32, nullable) receives the bank slot or -1. */
 int pr_sink_retrieve(pr_sink_cache* c, int32_t block, const float* fp_raw_dev,
@@ -177,7 +183,8 @@ int pr_sink_bank_state(pr_sink_cache* c, int32_t* ids_host, double* fp_host,
  * passed in; t_pad (a multiple of 64; the padding rows are zero) goes to
  * *t_pad_out.  The rotated K holds the keys rotated at the slot's place as of
  * the last block opened (a bank entry: at the Dynamic Sink's place); k_rot_dev
- * may be NULL. */
+ * may be NULL.  PR_SINK_SLOT_DYNAMIC is rejected (PR_SINK_EINVAL): view the
+ * bank entry the open block retrieved instead. */
 int pr_sink_slot_view(const pr_sink_cache* c, int32_t slot, int32_t layer, void** k_dev,
                       void** v_dev, void** k_rot_dev, int32_t* t_pad_out);
 

@@ -40,7 +40,7 @@ def test_arena_bytes_closed_form():
     for cfg in (synth.C0_TINY, synth.C1_480, synth.C2_384x672, synth.C4_STREAM_672x384):
         esz = 2 if cfg.dtype == synth.DTYPE_BF16 else 4
         pad = lambda n: -(-n // 64) * 64
-        slots = 2 + cfg.window_slots + cfg.bank_size
+        slots = 1 + cfg.window_slots + cfg.bank_size  # Static, window, bank (Dynamic reads a bank entry)
         row = cfg.n_heads * cfg.head_dim * esz
         # every slot holds raw K, V and rotated K per layer; plus the current
         # block's rotated K

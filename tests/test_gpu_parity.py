@@ -53,13 +53,17 @@ def check_rotations(cache, orc, cfg, layer, ref_k, block_k, kinds=None):
     W = cfg.window_slots
     segs = orc.segment_layout()
     dyn_t = segs[2][2]
-    slot_of = {O.SEG_REF: binding.SLOT_REF, O.SEG_STATIC: binding.SLOT_STATIC,
-               O.SEG_DYNAMIC: binding.SLOT_DYNAMIC}
+    slot_of = {O.SEG_REF: binding.SLOT_REF, O.SEG_STATIC: binding.SLOT_STATIC}
     places = []
     for kind, bid, t_start, n_frames, present in segs:
         if not present or kind == O.SEG_CURRENT or (kinds and kind not in kinds):
             continue
-        slot = binding.SLOT_WINDOW0 + bid % W if kind == O.SEG_WINDOW else slot_of[kind]
+        if kind == O.SEG_WINDOW:
+            slot = binding.SLOT_WINDOW0 + bid % W
+        elif kind == O.SEG_DYNAMIC:  # the Dynamic Sink reads the retrieved bank entry in place
+            slot = cache.slot_index_bank(orc.bank_ids.index(bid))
+        else:
+            slot = slot_of[kind]
         places.append((slot, bid, t_start, n_frames))
     if not kinds or "bank" in kinds:
         for i, bid in enumerate(orc.bank_ids):
@@ -335,6 +339,10 @@ def test_device_errors_leave_state_unchanged():
         cache.attend(0, to_dev(k, dt), to_dev(k, dt), to_dev(v, dt))  # wrong token count
     ids, _, misc = cache.bank_state()
     assert misc[0] == -1 and (ids == -1).all()
+    # the Dynamic Sink is a reference to a bank entry, not a slot: no view of it
+    with pytest.raises(binding.PRSinkError) as e:
+        cache.slot_view(binding.SLOT_DYNAMIC, 0)
+    assert e.value.code == binding.PR_SINK_EINVAL
 
 
 def test_footprint_constant_over_stream():
