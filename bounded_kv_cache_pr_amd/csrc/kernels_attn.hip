@@ -603,11 +603,12 @@ struct Attn {
       __builtin_amdgcn_raw_buffer_store_b64(ml, r, 256 * D * 4 + ((wave * 2 + qb) * 64 + lane) * 8, 0, kCoherent);
     }
   }
-  // Folds another piece of the same job into the registers: both sides are
-  // rescaled to the larger reference max.  All of the record's loads are
-  // issued before any is used (coherent loads are not reordered, so waiting
-  // on each in turn would pay the memory latency once per load).
-  __device__ void merge_partial(float* rec) {
+  // Folds another piece of the same job into the registers (first: replaces
+  // them): both sides are rescaled to the larger reference max.  All of the
+  // record's loads are issued before any is used (coherent loads are not
+  // reordered, so waiting on each in turn would pay the memory latency once
+  // per load).
+  __device__ void merge_partial(float* rec, bool first) {
     const __amdgpu_buffer_rsrc_t r = record(rec);
     u32x2 ml[2];
     u32x4 v[2][NDB][4];
@@ -624,6 +625,17 @@ struct Attn {
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
       const float mq = __uint_as_float(ml[qb].x), lq = __uint_as_float(ml[qb].y);
+      if (first) {
+        m_run[qb] = mq;
+        l_run[qb] = lq;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+          for (int g = 0; g < 4; ++g)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) o[qb][db][4 * g + e] = __uint_as_float(v[qb][db][g][e]);
+        continue;
+      }
       const float mx = fmaxf(m_run[qb], mq);
       const float al = __builtin_amdgcn_exp2f(m_run[qb] - mx), be = __builtin_amdgcn_exp2f(mq - mx);
       m_run[qb] = mx;
@@ -1033,8 +1045,9 @@ void attn_bf16_kernel(const AttnParams p) {
                                                  "") == (uint32_t)(w.n_pieces - 1);
     __syncthreads();
     if (!last_piece) return;
-    for (int r = 0; r < w.n_pieces; ++r)
-      if (r != w.piece) a.merge_partial(base + (size_t)r * rec);
+    // rebuilt from every record in piece order, this one's included, so the
+    // result does not depend on which piece arrived last
+    for (int r = 0; r < w.n_pieces; ++r) a.merge_partial(base + (size_t)r * rec, r == 0);
   }
   a.epilogue(qt);
 }

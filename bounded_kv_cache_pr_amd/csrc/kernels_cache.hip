@@ -1,5 +1,7 @@
 // Cache-maintenance kernels of the PR-Sink path on gfx950:
 //   kv_write     raw K/V [T][H][d] -> slot layout [t_pad][H][d] (contiguous copy)
+//   clean_write  the same for a closing block's clean K/V, plus its keys
+//                rotated at the place they take next
 //   rope_follow  raw keys -> keys rotated at a segment's current positions
 //   slot_copy    the first bytes of a block slot (all layers) -> another slot;
 //                source and destination come from device state, so no host
@@ -73,6 +75,30 @@ __device__ inline uint32_t pack_bf16(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
+// Chunk c (16 bytes: 4 bf16 pairs or 2 fp32 pairs) of one head row of a key
+// at position (tt, y, x), rotated.
+__device__ inline uint4 rotate_chunk(const RopeGeom& g, uint4 w, uint32_t c, int elem, int tt, int y, int x) {
+  if (elem == 2) {
+    uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float2 cs = rope_cs(g, (int)c * 4 + e, tt, y, x);
+      const float x0 = bf16_lo(ws[e]), x1 = bf16_hi(ws[e]);
+      ws[e] = pack_bf16(x0 * cs.x - x1 * cs.y, x0 * cs.y + x1 * cs.x);
+    }
+    return make_uint4(ws[0], ws[1], ws[2], ws[3]);
+  }
+  float f[4] = {__uint_as_float(w.x), __uint_as_float(w.y), __uint_as_float(w.z), __uint_as_float(w.w)};
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    const float2 cs = rope_cs(g, (int)c * 2 + e, tt, y, x);
+    const float x0 = f[2 * e], x1 = f[2 * e + 1];
+    f[2 * e] = x0 * cs.x - x1 * cs.y;
+    f[2 * e + 1] = x0 * cs.y + x1 * cs.x;
+  }
+  return make_uint4(__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]), __float_as_uint(f[3]));
+}
+
 __global__ __launch_bounds__(256) void rope_follow_kernel(const RotParams p) {
   const RotJob& jb = p.job[blockIdx.z];
   const size_t lay = (size_t)blockIdx.y * p.layer_bytes;
@@ -94,30 +120,40 @@ __global__ __launch_bounds__(256) void rope_follow_kernel(const RotParams p) {
     const uint32_t c = (i - n * per_tok) % per_head;
     int tt, y, x;
     token_pos(p.g, (int)n, jb.t_index, tt, y, x);
-    uint4 w = reinterpret_cast<const uint4*>(src)[i];
-    if (p.elem == 2) {
-      uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+    reinterpret_cast<uint4*>(dst)[i] = rotate_chunk(p.g, reinterpret_cast<const uint4*>(src)[i], c, p.elem, tt, y, x);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// clean_write: the clean K/V of one layer of the block being closed go to its
+// window slot, raw, together with the keys rotated at the place the block
+// takes when the next block opens (the newest window place); for block 0 the
+// same three tensors also go to the Static Sink, rotated at its place.  One
+// pass reads the clean keys once.  Thread = one 16-byte chunk of K and of V.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void clean_write_kernel(const CleanWrite p) {
+  const uint32_t per_head = (uint32_t)(p.head_dim * p.elem / 16);
+  const uint32_t per_tok = per_head * (uint32_t)p.n_heads;
+  const uint32_t total = per_tok * (uint32_t)p.n_tok;
+  const uint32_t stride = gridDim.x * 256;
+  const uint4* __restrict__ ks = reinterpret_cast<const uint4*>(p.k_src);
+  const uint4* __restrict__ vs = reinterpret_cast<const uint4*>(p.v_src);
+  for (uint32_t i = blockIdx.x * 256 + threadIdx.x; i < total; i += stride) {
+    const uint32_t n = i / per_tok;
+    const uint32_t c = (i - n * per_tok) % per_head;
+    const uint4 k = ks[i], v = vs[i];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float2 cs = rope_cs(p.g, (int)c * 4 + e, tt, y, x);
-        const float x0 = bf16_lo(ws[e]), x1 = bf16_hi(ws[e]);
-        ws[e] = pack_bf16(x0 * cs.x - x1 * cs.y, x0 * cs.y + x1 * cs.x);
+    for (int d = 0; d < 2; ++d) {
+      const CleanDst& o = p.dst[d];
+      if (!o.k) continue;
+      reinterpret_cast<uint4*>(o.k)[i] = k;
+      reinterpret_cast<uint4*>(o.v)[i] = v;
+      if (o.k_rot) {
+        int tt, y, x;
+        token_pos(p.g, (int)n, o.t_index, tt, y, x);
+        reinterpret_cast<uint4*>(o.k_rot)[i] = rotate_chunk(p.g, k, c, p.elem, tt, y, x);
       }
-      w = make_uint4(ws[0], ws[1], ws[2], ws[3]);
-    } else {
-      float f[4] = {__uint_as_float(w.x), __uint_as_float(w.y), __uint_as_float(w.z),
-                    __uint_as_float(w.w)};
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const float2 cs = rope_cs(p.g, (int)c * 2 + e, tt, y, x);
-        const float x0 = f[2 * e], x1 = f[2 * e + 1];
-        f[2 * e] = x0 * cs.x - x1 * cs.y;
-        f[2 * e + 1] = x0 * cs.y + x1 * cs.x;
-      }
-      w = make_uint4(__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]),
-                     __float_as_uint(f[3]));
     }
-    reinterpret_cast<uint4*>(dst)[i] = w;
   }
 }
 
@@ -259,6 +295,14 @@ hipError_t launch_rope_follow(const RotParams& p, int n_layers, hipStream_t s) {
   if (blocks > cap) blocks = cap;
   hipLaunchKernelGGL(rope_follow_kernel, dim3((unsigned)blocks, (unsigned)n_layers, (unsigned)p.n_jobs),
                      dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_clean_write(const CleanWrite& p, hipStream_t s) {
+  const size_t total = (size_t)p.n_tok * p.n_heads * p.head_dim * p.elem / 16;
+  size_t blocks = (total + 255) / 256;
+  if (blocks > 256 * 8) blocks = 256 * 8;
+  hipLaunchKernelGGL(clean_write_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 

@@ -203,6 +203,27 @@ struct pr_sink_cache {
   std::vector<uint8_t> ref_set, written;
   int n_cu;           // compute units of the device
 
+  // Cross-stream order.  Every call may use its own stream; an event marks
+  // each producer, and a consumer's stream waits on it only when the
+  // producer ran on another stream (same stream: queue order suffices).
+  struct Mark {
+    hipEvent_t ev = nullptr;
+    hipStream_t st = nullptr;
+    bool set = false;
+  };
+  std::vector<Mark> clean;  // per layer: the last clean write of that layer
+  Mark ref;                 // the last Ref Sink write
+  Mark attn;                // the last attention call
+  Mark retr;                // the last retrieval
+  Mark bank;                // the last bank update that wrote the bank
+  Mark done[2];             // block b's clean writes all complete, at [b & 1]
+
+  ~pr_sink_cache() {
+    auto drop = [](Mark& m) { if (m.ev) (void)hipEventDestroy(m.ev); };
+    for (Mark& m : clean) drop(m);
+    drop(ref); drop(attn); drop(retr); drop(bank); drop(done[0]); drop(done[1]);
+  }
+
   char* block_slot(int bs) const { return arena + lay.off_blocks + (size_t)bs * lay.slot_b; }
   char* ref_slot() const { return arena + lay.off_ref; }
   // raw K, V and rotated K of one layer inside a slot whose tensors are kv bytes
@@ -299,6 +320,18 @@ size_t block_bytes(const pr_sink_cache* c, int n_tok) {
   return (size_t)n_tok * c->cfg.n_heads * c->cfg.head_dim * c->lay.elem;
 }
 
+// Stream s waits for producer m if m ran on another stream.
+hipError_t after(hipStream_t s, const pr_sink_cache::Mark& m) {
+  if (!m.set || m.st == s) return hipSuccess;
+  return hipStreamWaitEvent(s, m.ev, 0);
+}
+// Marks the work queued so far on s as producer m.
+hipError_t mark(hipStream_t s, pr_sink_cache::Mark& m) {
+  m.st = s;
+  m.set = true;
+  return hipEventRecord(m.ev, s);
+}
+
 }  // namespace
 
 extern "C" {
@@ -348,6 +381,18 @@ int pr_sink_cache_init(const pr_sink_config* cfg, void* arena_dev, size_t arena_
   c->bank_count = 0;
   c->dyn_present = false;
   c->n_cu = n_cu;
+  c->clean.resize(cfg->n_layers);
+  if (!dry) {
+    auto make = [](pr_sink_cache::Mark& m) { return hipEventCreateWithFlags(&m.ev, hipEventDisableTiming); };
+    hipError_t e = hipSuccess;
+    for (auto& m : c->clean) if (e == hipSuccess) e = make(m);
+    for (auto* m : {&c->ref, &c->attn, &c->retr, &c->bank, &c->done[0], &c->done[1]})
+      if (e == hipSuccess) e = make(*m);
+    if (e != hipSuccess) {
+      delete c;
+      return fail(PR_SINK_EHIP, "hipEventCreateWithFlags: %s", hipGetErrorString(e));
+    }
+  }
   c->ref_set.assign(cfg->n_layers, 0);
   c->written.assign(cfg->n_layers, 0);
   *out = c;
@@ -365,12 +410,14 @@ int pr_sink_set_ref(pr_sink_cache* c, int32_t layer, const void* k_raw, const vo
     const Layout& L = c->lay;
     hipStream_t s = as_stream(stream);
     char* ref = c->ref_slot();
+    PRS_HIP(after(s, c->attn));  // earlier attention read the old Ref Sink
     PRS_HIP(launch_kv_write(k_raw, v_raw, ref + c->k_off(layer, L.kv_r), ref + c->v_off(layer, L.kv_r),
                             nullptr, nullptr, block_bytes(c, L.tr), s));
     // the Ref Sink's place never moves: rotate its keys once
     RotParams r = rot_params(c, L.tr, L.kv_r);
     add_job(r, ref + c->k_off(layer, L.kv_r), ref + c->r_off(layer, L.kv_r), 0);
     PRS_HIP(launch_rope_follow(r, 1, s));
+    PRS_HIP(mark(s, c->ref));
   }
   c->ref_set[layer] = 1;
   return PR_SINK_OK;
@@ -393,24 +440,29 @@ int pr_sink_retrieve(pr_sink_cache* c, int32_t block, const float* fp_raw_dev,
     const pr_sink_config& g = c->cfg;
     const Layout& L = c->lay;
     hipStream_t s = as_stream(stream);
+    // the bank state and entries of the last bank update; the raw keys of the
+    // window blocks that move (block-2 and older, written by the time block-2
+    // closed); the previous block's attention, which read the state and the
+    // rotated keys rewritten here
+    PRS_HIP(after(s, c->bank));
+    if (block >= 2) PRS_HIP(after(s, c->done[block & 1]));
+    PRS_HIP(after(s, c->attn));
     // r lands in the device state; attention reads bank entry r in place (its
     // K is kept rotated at the Dynamic Sink's place), so nothing is copied
     PRS_HIP(launch_retrieve(fp_raw_dev, c->phi_cur(), c->phi_bank(), c->state(), g.fp_dim,
                             c->bank_count, block, slot_out_dev, s));
-    // RoPE follow for the blocks whose place changes as this block opens: every
-    // previous window block moves one place, and block 0 becomes the Static Sink.
+    // RoPE follow for the window blocks that move one place as this block
+    // opens.  The previous block's keys are already at the newest window
+    // place, and block 0's at the Static Sink's: clean_kv_write rotated them.
     RotParams r = rot_params(c, L.tb, L.kv_b);
-    for (int j = 0; j < g.window_slots - 1; ++j) {
+    for (int j = 0; j < g.window_slots - 2; ++j) {
       const int id = block - (g.window_slots - 1) + j;
       if (id < 0) continue;
       char* w = c->block_slot(c->bs_window(id % g.window_slots));
       add_job(r, w + c->k_off(0, L.kv_b), w + c->r_off(0, L.kv_b), g.ref_frames + (2 + j) * g.block_frames);
     }
-    if (block == 1) {
-      char* st = c->block_slot(c->bs_static());
-      add_job(r, st + c->k_off(0, L.kv_b), st + c->r_off(0, L.kv_b), g.ref_frames);
-    }
     if (r.n_jobs) PRS_HIP(launch_rope_follow(r, g.n_layers, s));
+    PRS_HIP(mark(s, c->retr));
   }
   c->dyn_present = candidate;
   c->open = true;
@@ -434,6 +486,13 @@ int pr_sink_attend(pr_sink_cache* c, int32_t layer, const void* q_raw, const voi
   segment_table(c, tokens, t_index);
   const int n_seg = g.window_slots + 3;
   hipStream_t st = as_stream(stream);
+  // this layer's newest window block (the previous block's clean write), the
+  // retrieval, the Ref Sink, and the previous call (attention calls share the
+  // rotated-current-key scratch and the split-job records)
+  PRS_HIP(after(st, c->clean[layer]));
+  PRS_HIP(after(st, c->retr));
+  PRS_HIP(after(st, c->ref));
+  PRS_HIP(after(st, c->attn));
   // the current block's keys, rotated at the current positions
   char* cur_rot = c->arena + L.off_cur_rot;
   {
@@ -488,6 +547,7 @@ int pr_sink_attend(pr_sink_cache* c, int32_t layer, const void* q_raw, const voi
   p.part = L.n_part_rec ? reinterpret_cast<float*>(c->arena + L.off_part) : nullptr;
   p.cnt = L.n_cnt ? reinterpret_cast<uint32_t*>(c->arena + L.off_cnt) : nullptr;
   PRS_HIP(launch_attention(p, g.dtype, g.head_dim, c->n_cu, st));
+  PRS_HIP(mark(st, c->attn));
   return PR_SINK_OK;
 }
 
@@ -501,12 +561,32 @@ int pr_sink_clean_kv_write(pr_sink_cache* c, int32_t layer, const void* k_raw, c
   if (!c->dry) {
     const Layout& L = c->lay;
     const int b = c->next_block;
-    char* w = c->block_slot(c->bs_window(b % c->cfg.window_slots));
-    char* st = b == 0 ? c->block_slot(c->bs_static()) : nullptr;
-    PRS_HIP(launch_kv_write(k_raw, v_raw, w + c->k_off(layer, L.kv_b), w + c->v_off(layer, L.kv_b),
-                            st ? st + c->k_off(layer, L.kv_b) : nullptr,
-                            st ? st + c->v_off(layer, L.kv_b) : nullptr, block_bytes(c, L.tb),
-                            as_stream(stream)));
+    const pr_sink_config& g = c->cfg;
+    char* w = c->block_slot(c->bs_window(b % g.window_slots));
+    CleanWrite cw{};
+    cw.k_src = static_cast<const char*>(k_raw);
+    cw.v_src = static_cast<const char*>(v_raw);
+    cw.g = rope_geom(c);
+    cw.n_tok = L.tb;
+    cw.n_heads = g.n_heads;
+    cw.head_dim = g.head_dim;
+    cw.elem = L.elem;
+    // the window slot, with the keys rotated at the newest window place, the
+    // one this block takes when the next block opens (no window place to
+    // take when the window holds only the current block)
+    cw.dst[0] = {w + c->k_off(layer, L.kv_b), w + c->v_off(layer, L.kv_b),
+                 g.window_slots >= 2 ? w + c->r_off(layer, L.kv_b) : nullptr,
+                 g.ref_frames + g.window_slots * g.block_frames};
+    if (b == 0) {  // block 0 is also the Static Sink, from block 1 on
+      char* st = c->block_slot(c->bs_static());
+      cw.dst[1] = {st + c->k_off(layer, L.kv_b), st + c->v_off(layer, L.kv_b), st + c->r_off(layer, L.kv_b),
+                   g.ref_frames};
+    }
+    // the window slot last held block b-W, which the previous block attended
+    hipStream_t s = as_stream(stream);
+    PRS_HIP(after(s, c->attn));
+    PRS_HIP(launch_clean_write(cw, s));
+    PRS_HIP(mark(s, c->clean[layer]));
   }
   c->written[layer] = 1;
   return PR_SINK_OK;
@@ -518,9 +598,16 @@ int pr_sink_bank_update(pr_sink_cache* c, int32_t block, void* stream) {
   for (int l = 0; l < c->cfg.n_layers; ++l)
     if (!c->written[l]) return fail(PR_SINK_ESTATE, "clean K/V of layer %d not written for block %d", l, block);
   const pr_sink_config& g = c->cfg;
+  hipStream_t s = as_stream(stream);
+  if (!c->dry) {
+    // every clean write of this block (the bank copies the window slot, and
+    // the block's completion mark covers them), and its attention (which read
+    // bank entries as the Dynamic Sink)
+    for (auto& m : c->clean) PRS_HIP(after(s, m));
+    PRS_HIP(after(s, c->attn));
+  }
   if (block < g.bank_fill_blocks) {
     if (!c->dry) {
-      hipStream_t s = as_stream(stream);
       const Layout& L = c->lay;
       const int ws = c->bs_window(block % g.window_slots);
       PRS_HIP(launch_bank_update(c->phi_cur(), c->phi_bank(), c->state(), g.fp_dim, g.bank_size,
@@ -533,9 +620,11 @@ int pr_sink_bank_update(pr_sink_cache* c, int32_t block, void* stream) {
       r.job[0].from_state = 1;
       r.job[0].dst_off = (int64_t)c->r_off(0, L.kv_b);
       PRS_HIP(launch_rope_follow(r, g.n_layers, s));
+      PRS_HIP(mark(s, c->bank));
     }
     if (c->bank_count < g.bank_size) ++c->bank_count;
   }
+  if (!c->dry) PRS_HIP(mark(s, c->done[block & 1]));
   c->open = false;
   c->next_block = block + 1;
   return PR_SINK_OK;
@@ -547,6 +636,9 @@ int pr_sink_bank_state(pr_sink_cache* c, int32_t* ids_host, double* fp_host, int
   if (!ids_host) return fail(PR_SINK_EINVAL, "ids_host is NULL");
   if (c->dry) return fail(PR_SINK_EINVAL, "dry-run cache has no device state");
   hipStream_t s = as_stream(stream);
+  // the state is written by retrievals and bank updates, possibly on other streams
+  PRS_HIP(after(s, c->retr));
+  PRS_HIP(after(s, c->bank));
   DevState st;
   PRS_HIP(hipMemcpyAsync(&st, c->state(), sizeof st, hipMemcpyDeviceToHost, s));
   if (fp_host)

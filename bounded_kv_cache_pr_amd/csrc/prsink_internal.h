@@ -158,12 +158,30 @@ struct RotParams {
   int32_t n_jobs, n_tok, n_heads, head_dim, elem;
 };
 
+// One destination of a clean write: raw K, V and (k_rot != nullptr) K rotated
+// at the place whose first frame has temporal row t_index.  k == nullptr:
+// unused.
+struct CleanDst {
+  char* k;
+  char* v;
+  char* k_rot;
+  int32_t t_index;
+};
+struct CleanWrite {
+  const char* k_src;    // clean K of one layer, [n_tok][H][d]
+  const char* v_src;
+  CleanDst dst[2];      // the window slot; the Static Sink (block 0 only)
+  RopeGeom g;
+  int32_t n_tok, n_heads, head_dim, elem;
+};
+
 // Launchers (kernels_*.hip).  All return the launch status.
 // n_cu: compute units of the device (sizes the work split of the bf16 kernel).
 hipError_t launch_attention(const AttnParams& p, int dtype, int head_dim, int n_cu, hipStream_t s);
 hipError_t launch_rope_follow(const RotParams& p, int n_layers, hipStream_t s);
 hipError_t launch_kv_write(const void* k_src, const void* v_src, void* k_dst0, void* v_dst0,
                            void* k_dst1, void* v_dst1, size_t bytes, hipStream_t s);
+hipError_t launch_clean_write(const CleanWrite& p, hipStream_t s);
 hipError_t launch_slot_copy(char* block_base, size_t slot_bytes, size_t copy_bytes,
                             const DevState* st, hipStream_t s);
 hipError_t launch_retrieve(const float* fp_raw, double* phi_cur, const double* bank_phi,

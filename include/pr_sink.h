@@ -40,8 +40,16 @@
  * Streams: every call is asynchronous on `stream` (a hipStream_t passed as
  * void*; NULL = the null stream) except pr_sink_cache_init and
  * pr_sink_bank_state, which synchronise.  Inputs must stay valid until the
- * work queued on `stream` has run.  One cache must not be driven from two
- * threads or two streams at once.
+ * work queued on `stream` has run.  Calls may use different streams: the
+ * library orders them with events (a stream waits only on work queued on
+ * another stream that it depends on), so results do not depend on the
+ * streams chosen.  The intended split (review, discussion of the Clean KV
+ * Update's 24 % share: overlap it) puts pr_sink_clean_kv_write and
+ * pr_sink_bank_update on a second stream: block b+1's attention of layer l
+ * then waits only for block b's clean write of layer l, and from the frozen
+ * bank on (block >= bank_fill_blocks) retrieval waits for no clean write of
+ * the block just closed.  The calls themselves must come from one host
+ * thread, in the block order below.
  *
  * Call order per block b = 0, 1, 2, ...:
  *   pr_sink_retrieve(b)  ->  pr_sink_attend(layer) any number of times
@@ -138,7 +146,8 @@ int pr_sink_set_ref(pr_sink_cache* c, int32_t layer, const void* k_raw, const vo
  * device (the host never waits for the retrieval).  The entry cannot change
  * while the block is open: the bank is written only by pr_sink_bank_update.
  * If no entry is eligible the Dynamic Sink is not attended during this block.
- * Also re-rotates the keys of the blocks whose place changes as block opens.
+ * Also re-rotates the keys of the window blocks that move one place as the
+ * block opens (the previous block's keys were rotated by its clean write).
  * slot_out_dev (device int32, nullable) receives the bank slot or -1. */
 int pr_sink_retrieve(pr_sink_cache* c, int32_t block, const float* fp_raw_dev,
                      int32_t* slot_out_dev, void* stream);
@@ -157,7 +166,11 @@ int pr_sink_attend(pr_sink_cache* c, int32_t layer, const void* q_raw, const voi
 /* Clean KV Update, write half: stores the clean raw K/V of the open block for
  * `layer` (device, [T][H][d]) into its rolling-window slot, and for block 0
  * also into the Static Sink (review, full-pipeline paragraph; HF abstract:
- * Static Sink = first generated block).  Once per layer per block. */
+ * Static Sink = first generated block).  In the same pass it stores the keys
+ * rotated at the place the block takes when the next block opens (the newest
+ * window place; block 0 also at the Static Sink's place), so that opening
+ * the next block re-rotates only the window blocks that move again.  Once
+ * per layer per block. */
 int pr_sink_clean_kv_write(pr_sink_cache* c, int32_t layer, const void* k_raw,
                            const void* v_raw, void* stream);
 

@@ -160,3 +160,67 @@ def test_stream_672x384_240_blocks():
     log("case: 672x384 stream, 240 blocks, recurring motifs, seed 4")
     fps = synth.pose_stream(synth.STREAM_BLOCKS["C4"], n_protos=12, seed=4, motifs=True)
     run_stream("672x384", cfg, synth.STREAM_BLOCKS["C4"], fps, seed=4)
+
+
+def _clean_path_stream(cfg, fps, two_streams, full_blocks):
+    """One stream of len(fps) blocks; with two_streams the clean-KV path
+    (clean writes, bank update) runs on a second stream.  Returns the
+    per-call checksums, the full outputs of full_blocks, the bank state and
+    every stored slot."""
+    L, S = cfg.n_layers, synth.DENOISE_STEPS
+    s1 = torch.cuda.current_stream(DEV)
+    s2 = torch.cuda.Stream(DEV) if two_streams else s1
+    cache = binding.PRSinkCache(cfg, device=DEV)
+    for l in range(L):
+        cache.set_ref(l, *synth.ref_kv_torch(cfg, l, 6, DEV))
+    qkv_pool = [synth.step_qkv_torch(cfg, 70_000 + i, 0, 0, 6, DEV) for i in range(POOL)]
+    clean_pool = [synth.clean_kv_torch(cfg, 80_000 + i, 0, 6, DEV) for i in range(POOL)]
+    torch.cuda.synchronize()
+    fps_dev = torch.from_numpy(fps).to(DEV)
+    out = torch.empty_like(qkv_pool[0][0])
+    w = torch.arange(out.numel(), device=DEV, dtype=torch.int64) % 65521
+    sums, kept = [], {}
+    for b in range(len(fps)):
+        cache.retrieve(b, fps_dev[b])
+        for s in range(S):
+            for l in range(L):
+                q, k, v = qkv_pool[(b * S * L + s * L + l) % POOL]
+                cache.attend(l, q, k, v, out=out)
+                x = out.view(torch.int16).reshape(-1).to(torch.int64)  # on s1, after the call
+                sums.append(torch.stack([x.sum(), (x * w).sum()]))
+                if b in full_blocks:
+                    kept[(b, s, l)] = out.clone()
+        with torch.cuda.stream(s2):
+            for l in range(L):
+                cache.clean_kv_write(l, *clean_pool[(b * L + l) % POOL])
+            cache.bank_update(b)
+    torch.cuda.synchronize()
+    ids, phi, misc = cache.bank_state()
+    slots = {}
+    for slot in [binding.SLOT_STATIC] + [binding.SLOT_WINDOW0 + j for j in range(cfg.window_slots)] + \
+            [cache.slot_index_bank(i) for i in range(cfg.bank_size)]:
+        for l in range(L):
+            slots[(slot, l)] = tuple(t.clone() for t in cache.slot_view(slot, l, rotated=True))
+    return torch.stack(sums).cpu(), kept, (ids, phi, misc), slots
+
+
+def test_clean_path_on_second_stream_matches_one_stream():
+    """Clean writes and bank updates on a second stream, ordered by the
+    library's events: the next block's attention of layer l waits only for
+    that layer's clean write.  Everything equals a one-stream run bit for
+    bit, across the bank freeze (block 20) and the window ring."""
+    cfg = synth.PRSinkConfig(n_layers=4, n_heads=8, head_dim=128, rope_dims=(44, 42, 42),
+                             rope_theta=1e4, lat_h=16, lat_w=16, ref_frames=1, block_frames=3)
+    log("case: clean path on a second stream, 26 blocks, T=768, H=8")
+    fps = synth.pose_stream(26, n_protos=8, seed=6)
+    full = {1, 2, 19, 20, 21, 25}
+    a = _clean_path_stream(cfg, fps, False, full)
+    b = _clean_path_stream(cfg, fps, True, full)
+    assert torch.equal(a[0], b[0]), "attention checksums differ between one and two streams"
+    for key in a[1]:
+        assert torch.equal(a[1][key], b[1][key]), f"output {key} differs"
+    for x, y in zip(a[2], b[2]):
+        assert np.array_equal(x, y), "bank state differs"
+    for key in a[3]:
+        for x, y in zip(a[3][key], b[3][key]):
+            assert torch.equal(x, y), f"slot {key} differs"
