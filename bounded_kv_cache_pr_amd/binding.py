@@ -22,7 +22,8 @@ SLOT_REF, SLOT_STATIC, SLOT_DYNAMIC, SLOT_WINDOW0 = 0, 1, 2, 3
 EXPORTED = (
     "pr_sink_arena_bytes", "pr_sink_cache_init", "pr_sink_set_ref", "pr_sink_retrieve",
     "pr_sink_attend", "pr_sink_clean_kv_write", "pr_sink_bank_update", "pr_sink_bank_state",
-    "pr_sink_slot_view", "pr_sink_segments", "pr_sink_cache_destroy", "pr_sink_last_error",
+    "pr_sink_slot_view", "pr_sink_segments", "pr_sink_set_attend_events", "pr_sink_cache_destroy",
+    "pr_sink_last_error",
 )
 
 
@@ -72,6 +73,7 @@ def lib() -> ctypes.CDLL:
             "pr_sink_slot_view": (i32, [vp, i32, i32, POINTER(vp), POINTER(vp), POINTER(vp),
                                         POINTER(i32)]),
             "pr_sink_segments": (i32, [vp, vp, vp, POINTER(i32)]),
+            "pr_sink_set_attend_events": (i32, [vp, vp, vp]),
             "pr_sink_cache_destroy": (i32, [vp]),
             "pr_sink_last_error": (ctypes.c_char_p, []),
         }
@@ -200,6 +202,12 @@ class PRSinkCache:
         check(lib().pr_sink_bank_state(self._h, ids.ctypes.data, phi.ctypes.data,
                                        misc.ctypes.data, self._stream()))
         return ids, phi, tuple(int(x) for x in misc)
+
+    def set_attend_events(self, start=None, stop=None):
+        """Records torch.cuda.Events (timing enabled, already created) around
+        every later attention kernel; no arguments turns it off."""
+        h = (lambda e: c_void_p(e.cuda_event) if e is not None else None)
+        check(lib().pr_sink_set_attend_events(self._h, h(start), h(stop)))
 
     def segments(self):
         """[(tokens, t_start)] of the open block in cache order."""

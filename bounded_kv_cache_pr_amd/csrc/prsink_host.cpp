@@ -217,6 +217,7 @@ struct pr_sink_cache {
   Mark retr;                // the last retrieval
   Mark bank;                // the last bank update that wrote the bank
   Mark done[2];             // block b's clean writes all complete, at [b & 1]
+  hipEvent_t time_start = nullptr, time_stop = nullptr;  // caller's events around the attention kernel
 
   ~pr_sink_cache() {
     auto drop = [](Mark& m) { if (m.ev) (void)hipEventDestroy(m.ev); };
@@ -546,7 +547,9 @@ int pr_sink_attend(pr_sink_cache* c, int32_t layer, const void* q_raw, const voi
   p.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)g.head_dim));
   p.part = L.n_part_rec ? reinterpret_cast<float*>(c->arena + L.off_part) : nullptr;
   p.cnt = L.n_cnt ? reinterpret_cast<uint32_t*>(c->arena + L.off_cnt) : nullptr;
+  if (c->time_start) PRS_HIP(hipEventRecord(c->time_start, st));
   PRS_HIP(launch_attention(p, g.dtype, g.head_dim, c->n_cu, st));
+  if (c->time_stop) PRS_HIP(hipEventRecord(c->time_stop, st));
   PRS_HIP(mark(st, c->attn));
   return PR_SINK_OK;
 }
@@ -694,6 +697,14 @@ int pr_sink_segments(const pr_sink_cache* c, int32_t* tokens_out, int32_t* t_sta
     t_start_out[s] = c->cfg.t0 + t_index[s];
   }
   *n_out = n;
+  return PR_SINK_OK;
+}
+
+int pr_sink_set_attend_events(pr_sink_cache* c, void* ev_start, void* ev_stop) {
+  if (!c) return fail(PR_SINK_EINVAL, "cache is NULL");
+  if ((ev_start == nullptr) != (ev_stop == nullptr)) return fail(PR_SINK_EINVAL, "set both events or neither");
+  c->time_start = static_cast<hipEvent_t>(ev_start);
+  c->time_stop = static_cast<hipEvent_t>(ev_stop);
   return PR_SINK_OK;
 }
 

@@ -201,6 +201,14 @@ int pr_sink_bank_state(pr_sink_cache* c, int32_t* ids_host, double* fp_host,
 int pr_sink_slot_view(const pr_sink_cache* c, int32_t slot, int32_t layer, void** k_dev,
                       void** v_dev, void** k_rot_dev, int32_t* t_pad_out);
 
+/* Measurement hook: with events set (hipEvent_t passed as void*, created by
+ * the caller with timing enabled), every later pr_sink_attend records
+ * ev_start on its stream right before its attention kernel and ev_stop right
+ * after it, so the kernel's own duration can be read without the rotation of
+ * the current keys that precedes it.  Both NULL turns it off.  The events
+ * stay owned by the caller and must outlive their use. */
+int pr_sink_set_attend_events(pr_sink_cache* c, void* ev_start, void* ev_stop);
+
 /* Segments of the open block in cache order (Ref, Static, Dynamic, W-1
  * window blocks oldest first, current): token counts (0 = not attended) and
  * temporal start of each, n_out receives the count (window_slots + 3). */
