@@ -44,6 +44,9 @@ class PRSinkConfig:
     fp_dim: int = 558
     dtype: str = DTYPE_BF16
     t0: int = 0
+    bank_policy: int = 0          # bits: 1 zero-fingerprint fallback, 2 continual, 4 gated refresh
+    bank_stale_blocks: int = 1    # continual: blocks unused before an entry may be evicted
+    bank_refresh_tau: float = 0.0  # gated: refresh when the best bank dot product is below this
 
     @property
     def tokens_per_frame(self) -> int:

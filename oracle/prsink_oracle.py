@@ -42,6 +42,23 @@ K/V of the block together with its driving fingerprint.
 Parity unpinned: the RoPE band split / pairing / frequency convention and the
 Ref Sink's temporal slot are this oracle's reading; the pages fix neither.
 They are pinned only to that stated reading (closed forms) and to invariants.
+
+Bank-policy variants (review, weaknesses paragraph: the frozen M = 5 bank is
+fragile; directions: continual writes with decaying weights, a bank refresh
+gated by fingerprint distance, and, when pose detection fails, falling back to
+the Static Sink + window).  The pages name the directions only; the readings,
+each off by default (policy 0 is the method as described):
+
+* ZERO_FALLBACK: a block whose fingerprint is all zero (every frame failed)
+  attends no Dynamic Sink and is never written into the bank.
+* CONTINUAL: an entry's weight halves every K = bank_stale_blocks blocks since
+  it was last written or retrieved; after the fill phase the exhaustive
+  replacement keeps running, but may only evict entries whose weight has
+  reached 1/2 (unused for at least K blocks).
+* GATED: after the fill phase, a block whose best dot product with the bank
+  (all entries) is below tau = bank_refresh_tau triggers the full exhaustive
+  replacement.
+Insertion: while the bank has room, an update inserts into the next slot.
 """
 from __future__ import annotations
 
@@ -51,6 +68,9 @@ import numpy as np
 
 SEG_REF, SEG_STATIC, SEG_DYNAMIC, SEG_WINDOW, SEG_CURRENT = (
     "ref", "static", "dynamic", "window", "current")
+
+# bank-policy bits
+POLICY_ZERO_FALLBACK, POLICY_CONTINUAL, POLICY_GATED = 1, 2, 4
 
 
 # ----------------------------------------------------------------------------
@@ -154,17 +174,20 @@ def mean_pairwise_similarity(phis) -> float:
     return tot / cnt
 
 
-def bank_decision(bank_phi, phi_b: np.ndarray, bank_size: int):
+def bank_decision(bank_phi, phi_b: np.ndarray, bank_size: int, evictable=None):
     """Diversity update of a bank that is being written.
 
     Returns ("insert", slot) while the bank has room, else ("keep", None) or
     ("swap", j): the option among [keep, swap 0, ..., swap M-1] with the
-    smallest mean in-bank similarity, the first one winning ties.
+    smallest mean in-bank similarity, the first one winning ties.  With
+    ``evictable`` (one flag per entry) only those entries may be swapped out.
     """
     if len(bank_phi) < bank_size:
         return ("insert", len(bank_phi))
     best, best_s = ("keep", None), mean_pairwise_similarity(bank_phi)
     for j in range(len(bank_phi)):
+        if evictable is not None and not evictable[j]:
+            continue
         cand = list(bank_phi)
         cand[j] = phi_b
         s = mean_pairwise_similarity(cand)
@@ -195,6 +218,8 @@ class PRSinkOracle:
         self.dynamic_id = None
         self.bank_ids = []
         self.bank_phi = []
+        self.bank_last_used = []  # block at which each entry was last written or retrieved
+        self.best_score = -math.inf  # the open block's best dot product with the bank
         self.phi_cur = None
         self.last_r = None
         self.last_decision = None
@@ -236,11 +261,18 @@ class PRSinkOracle:
         if self.is_open or block != self.next_block:
             raise RuntimeError("blocks must be opened in order, one at a time")
         self.phi_cur = fingerprint(fp_raw)
-        r = retrieve(self.phi_cur, self.bank_ids, self.bank_phi, block)
+        policy = getattr(self.cfg, "bank_policy", 0)
+        scores = retrieval_scores(self.phi_cur, self.bank_phi)
+        self.best_score = float(scores.max()) if len(scores) else -math.inf
+        if policy & POLICY_ZERO_FALLBACK and not np.any(self.phi_cur):
+            r = None  # no pose detected: Static Sink + window only
+        else:
+            r = retrieve(self.phi_cur, self.bank_ids, self.bank_phi, block)
         if r is None:
             self.dynamic_id = None
         else:
             self.dynamic_id = self.bank_ids[r]
+            self.bank_last_used[r] = block
         self.last_r = r
         self.is_open = True
         return r
@@ -303,14 +335,26 @@ class PRSinkOracle:
         if block == 0:
             self.static_id = 0
         self.last_decision = None
-        if block < c.bank_fill_blocks:
-            kind, slot = bank_decision(self.bank_phi, self.phi_cur, c.bank_size)
+        policy = getattr(c, "bank_policy", 0)
+        filling = block < c.bank_fill_blocks
+        if filling or policy & (POLICY_CONTINUAL | POLICY_GATED):
+            if policy & POLICY_ZERO_FALLBACK and not np.any(self.phi_cur):
+                kind, slot = "keep", None  # an undetected pose is never written
+            elif filling or (policy & POLICY_GATED and self.best_score < c.bank_refresh_tau):
+                kind, slot = bank_decision(self.bank_phi, self.phi_cur, c.bank_size)
+            else:  # continual writes: only entries unused for K blocks may go
+                K = c.bank_stale_blocks
+                stale = [block - t >= K for t in self.bank_last_used] if policy & POLICY_CONTINUAL \
+                    else [False] * len(self.bank_phi)
+                kind, slot = bank_decision(self.bank_phi, self.phi_cur, c.bank_size, stale)
             if kind == "insert":
                 self.bank_ids.append(block)
                 self.bank_phi.append(self.phi_cur.copy())
+                self.bank_last_used.append(block)
             elif kind == "swap":
                 self.bank_ids[slot] = block
                 self.bank_phi[slot] = self.phi_cur.copy()
+                self.bank_last_used[slot] = block
             self.last_decision = (kind, slot)
         self.is_open = False
         self.next_block = block + 1

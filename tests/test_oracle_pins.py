@@ -415,3 +415,140 @@ def test_block_order_is_enforced():
         orc.open_block(1, np.ones(558))
     with pytest.raises(RuntimeError):
         orc.close_block(1)
+
+
+# ---- bank-policy variants (review, weaknesses paragraph) ---------------------
+def _unit(*parts, n=558):
+    v = np.zeros(n)
+    for i, w in parts:
+        v[i] = w
+    return v / np.linalg.norm(v)
+
+
+def _policy_oracle(policy, K=1, tau=0.0, fill=5):
+    cfg = synth.C0_TINY.replace(bank_policy=policy, bank_stale_blocks=K, bank_refresh_tau=tau,
+                                bank_fill_blocks=fill)
+    return O.PRSinkOracle(cfg)
+
+
+def _step(orc, b, x):
+    r = orc.open_block(b, x)
+    return r, orc.close_block(b)
+
+
+# A bank of five entries: two near-duplicates (e0 and a unit vector 0.1 rad
+# away from it) and three orthogonal ones.  The far candidate is almost
+# orthogonal to all of them (0.01 towards entry 3, so its retrieval picks
+# entry 3 and leaves the duplicates' weights alone); it lowers the mean
+# similarity only if it replaces one of the duplicates, and the first one
+# (slot 0) wins the tie between the two.
+_DUP = [_unit((0, 1.0)), _unit((0, math.cos(0.1)), (1, math.sin(0.1))), _unit((2, 1.0)),
+        _unit((3, 1.0)), _unit((4, 1.0))]
+_FAR = _unit((10, 1.0), (3, 0.01))
+
+
+def _filled(policy, K=1, tau=0.0):
+    orc = _policy_oracle(policy, K, tau)
+    for b, x in enumerate(_DUP):
+        _step(orc, b, x)
+    assert orc.bank_ids == [0, 1, 2, 3, 4]
+    return orc
+
+
+def test_policy_frozen_by_default():
+    orc = _filled(0)
+    assert _step(orc, 5, _FAR)[1] is None  # past the fill phase: no update at all
+    assert orc.bank_ids == [0, 1, 2, 3, 4]
+
+
+def test_policy_continual_evicts_only_stale_entries():
+    # K = 3.  Retrieval counts as use: the fill-phase candidates are
+    # orthogonal to the bank, all their dots tie at 0 and the lowest eligible
+    # slot, entry 0, is retrieved at blocks 2, 3 and 4.  At block 5 entry 0 is
+    # therefore fresh (age 1) and the stale duplicate is entry 1 (written at
+    # block 1, never retrieved: age 4 >= 3)
+    orc = _filled(O.POLICY_CONTINUAL, K=3)
+    assert orc.bank_last_used == [4, 1, 2, 3, 4]
+    _, dec = _step(orc, 5, _FAR)
+    assert dec == ("swap", 1) and orc.bank_ids == [0, 5, 2, 3, 4]
+    # the same, but entries 0 and 1 were retrieved recently (blocks 5 and 6),
+    # so at block 7 neither duplicate may go (only orthogonal entries are
+    # stale, and swapping those does not help) and the bank keeps
+    orc = _filled(O.POLICY_CONTINUAL, K=3)
+    assert _step(orc, 5, _DUP[0])[0] == 0            # retrieves entry 0
+    assert _step(orc, 6, _DUP[1] + 1e-3 * _DUP[2])[0] == 1
+    _, dec = _step(orc, 7, _FAR)
+    assert dec == ("keep", None) and orc.bank_ids == [0, 1, 2, 3, 4]
+    # three blocks later entry 0 is stale again (age 10 - 5 = 5 >= 3): it goes
+    for b in (8, 9):
+        _step(orc, b, _DUP[4])                     # retrieves entry 4 only
+    _, dec = _step(orc, 10, _FAR)
+    assert dec == ("swap", 0)
+
+
+def test_policy_gated_refresh_by_fingerprint_distance():
+    # tau = 0.5: a candidate at cosine 0.6 from entry 2 does not trigger a
+    # refresh although a swap would help; one at distance (best dot 0) does
+    orc = _filled(O.POLICY_GATED, tau=0.5)
+    near = _unit((2, 0.6), (10, 0.8))
+    _, dec = _step(orc, 5, near)
+    assert dec == ("keep", None) and orc.bank_ids == [0, 1, 2, 3, 4]
+    _, dec = _step(orc, 6, _FAR)
+    assert dec == ("swap", 0) and orc.bank_ids == [6, 1, 2, 3, 4]
+
+
+def test_policy_zero_fingerprint_fallback():
+    zero = np.zeros(558)
+    # without the fallback an all-zero fingerprint retrieves the lowest
+    # eligible slot (all dots are 0) and is inserted while the bank fills
+    orc = _policy_oracle(0)
+    _step(orc, 0, _DUP[0])
+    _step(orc, 1, _DUP[2])
+    r, dec = _step(orc, 2, zero)
+    assert r == 0 and dec == ("insert", 2)
+    # with it: no Dynamic Sink, never written; the next detected pose takes
+    # the slot
+    orc = _policy_oracle(O.POLICY_ZERO_FALLBACK | O.POLICY_GATED, tau=0.5)
+    _step(orc, 0, _DUP[0])
+    _step(orc, 1, _DUP[2])
+    r, dec = _step(orc, 2, zero)
+    assert r is None and orc.dynamic_id is None and dec == ("keep", None)
+    _, dec = _step(orc, 3, _DUP[3])
+    assert dec == ("insert", 2) and orc.bank_ids == [0, 1, 3]
+    for b in (4, 5, 6):
+        _step(orc, b, _DUP[4 if b == 4 else 1])
+    assert len(orc.bank_ids) == 5
+    # gated refresh past the fill phase: a zero fingerprint (best dot 0 < tau)
+    # still never enters the bank
+    ids = list(orc.bank_ids)
+    r, dec = _step(orc, 7, zero)
+    assert r is None and dec == ("keep", None) and orc.bank_ids == ids
+
+
+def test_policy_invariants_over_a_long_stream():
+    """All three policies on a 60-block pose walk with zeroed frames: ids stay
+    distinct; an entry retrieved or written within the last K blocks is never
+    evicted by a continual write; zero fingerprints never enter the bank."""
+    K = 4
+    cfg = synth.C0_TINY.replace(bank_policy=7, bank_stale_blocks=K, bank_refresh_tau=0.9,
+                                bank_fill_blocks=8)
+    orc = O.PRSinkOracle(cfg)
+    fps = synth.pose_stream(60, n_protos=12, seed=11)
+    fps[[13, 14, 30]] = 0.0
+    used = {}
+    for b in range(60):
+        r = orc.open_block(b, fps[b])
+        if r is not None:
+            used[orc.bank_ids[r]] = b
+        before = list(orc.bank_ids)
+        gate = orc.best_score < cfg.bank_refresh_tau
+        dec = orc.close_block(b)
+        assert len(set(orc.bank_ids)) == len(orc.bank_ids)
+        if not np.any(fps[b]):
+            assert b not in orc.bank_ids and r is None
+        if dec and dec[0] == "swap" and b >= cfg.bank_fill_blocks and not gate:
+            gone = before[dec[1]]
+            last = max(used.get(gone, gone), gone)
+            assert b - last >= K, f"block {b} evicted entry of block {gone} used at {last}"
+        for bid in orc.bank_ids:
+            used.setdefault(bid, bid)
