@@ -34,6 +34,7 @@ class CConfig(ctypes.Structure):
         ("lat_h", c_int32), ("lat_w", c_int32), ("ref_frames", c_int32),
         ("block_frames", c_int32), ("window_slots", c_int32), ("bank_size", c_int32),
         ("bank_fill_blocks", c_int32), ("fp_dim", c_int32), ("dtype", c_int32), ("t0", c_int32),
+        ("bank_policy", c_int32), ("bank_stale_blocks", c_int32), ("bank_refresh_tau", c_double),
     ]
 
 
@@ -41,7 +42,8 @@ def to_c_config(cfg: PRSinkConfig) -> CConfig:
     return CConfig(cfg.n_layers, cfg.n_heads, cfg.head_dim, (c_int32 * 3)(*cfg.rope_dims),
                    float(cfg.rope_theta), cfg.lat_h, cfg.lat_w, cfg.ref_frames, cfg.block_frames,
                    cfg.window_slots, cfg.bank_size, cfg.bank_fill_blocks, cfg.fp_dim,
-                   0 if cfg.dtype == DTYPE_BF16 else 1, cfg.t0)
+                   0 if cfg.dtype == DTYPE_BF16 else 1, cfg.t0, cfg.bank_policy,
+                   cfg.bank_stale_blocks, float(cfg.bank_refresh_tau))
 
 
 class PRSinkError(RuntimeError):

@@ -196,14 +196,14 @@ struct SegCursor {
   int dyn_r;  // bank entry of the Dynamic Sink (load_dyn_r)
   __device__ __forceinline__ void seek(const AttnParams& p, size_t head_off, uint32_t tok_bytes,
                                        uint32_t tile_bytes, bool is_k) {
-    while (s < p.n_seg && p.seg[s].count < kKeyTile) ++s;
+    while (s < p.n_seg && seg_count(p, s, dyn_r) < kKeyTile) ++s;
     if (s < p.n_seg) {
       const char* base = seg_base(p, s, is_k, dyn_r) + head_off;
-      const int nrec = (int)((size_t)p.seg[s].count * tok_bytes - head_off);
+      const int nrec = (int)((size_t)seg_count(p, s, dyn_r) * tok_bytes - head_off);
       r = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), 0, nrec, 0x00020000);
       off = 0;
       step = tile_bytes;
-      left = p.seg[s].count / kKeyTile;
+      left = seg_count(p, s, dyn_r) / kKeyTile;
     } else {  // past the last tile: back onto it, and stay
       off -= step;
       step = 0;
@@ -219,7 +219,7 @@ struct SegCursor {
     int acc = 0, sel = -1, skip = 0;
 #pragma unroll
     for (int i = 0; i < kMaxSegments; ++i) {
-      const int n = p.seg[i].count / kKeyTile;
+      const int n = seg_count(p, i, dyn_r) / kKeyTile;
       if (sel < 0 && start < acc + n) {
         sel = i;
         skip = start - acc;
@@ -329,7 +329,7 @@ struct Attn {
     const char* row = nullptr;
 #pragma unroll
     for (int s = 0; s < kMaxSegments; ++s) {
-      const int cnt = p.seg[s].count, r = cnt % KT;
+      const int cnt = seg_count(p, s, dyn_r), r = cnt % KT;
       const char* base = seg_base(p, s, k, dyn_r);
       const char* cand = base + (size_t)head * D * 2 + (size_t)(cnt - r + kk - off) * tok_bytes;
       row = kk >= off && kk < off + r ? cand : row;
@@ -340,7 +340,7 @@ struct Attn {
   __device__ int ragged_keys() const {
     int r = 0;
 #pragma unroll
-    for (int s = 0; s < kMaxSegments; ++s) r += p.seg[s].count % KT;
+    for (int s = 0; s < kMaxSegments; ++s) r += seg_count(p, s, dyn_r) % KT;
     return r;
   }
 
@@ -407,7 +407,7 @@ struct Attn {
     const int si = valid ? s : 0;
     const Segment& sg = p.seg[si];
     const size_t off = valid ? (size_t)head * sg.head * 2 + (size_t)n0 * tok_bytes : 0;
-    const int nrec = valid ? (int)((size_t)(sg.count - n0) * tok_bytes) : 0;
+    const int nrec = valid ? (int)((size_t)(seg_count(p, si, dyn_r) - n0) * tok_bytes) : 0;
     rk = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(seg_base(p, si, true, dyn_r) + off), 0, nrec,
                                            kBufferConfig);
     rv = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(seg_base(p, si, false, dyn_r) + off), 0, nrec,
@@ -796,13 +796,16 @@ void attn_bf16_kernel(const AttnParams p) {
 
   int n_tiles = 0;  // full tiles of the head (unused segment slots have count 0)
 #pragma unroll
-  for (int s = 0; s < kMaxSegments; ++s) n_tiles += p.seg[s].count / A::KT;
+  for (int s = 0; s < kMaxSegments; ++s) n_tiles += seg_count(p, s, a.dyn_r) / A::KT;
   const int n_ragged = a.ragged_keys();
   // this piece's units [u0, u1): full tiles [f0, f0 + n_full), then packed
   // ragged tiles [pk0, pk1)
   const int u0 = p.units * w.piece / w.n_pieces, u1 = p.units * (w.piece + 1) / w.n_pieces;
   const int f0 = min(u0, n_tiles), n_full = min(u1, n_tiles) - f0;
-  const int pk0 = max(u0, n_tiles) - n_tiles, pk1 = max(u1, n_tiles) - n_tiles;
+  // (units counts the Dynamic segment as planned; a vanished one leaves fewer
+  // tiles than planned, so both ranges are clamped to what exists)
+  const int n_pk = (n_ragged + A::KT - 1) / A::KT;
+  const int pk0 = min(max(u0, n_tiles) - n_tiles, n_pk), pk1 = min(max(u1, n_tiles) - n_tiles, n_pk);
 
   bool bad = false;
   if (n_full > 0) {
@@ -1005,7 +1008,7 @@ void attn_bf16_kernel(const AttnParams p) {
   if (bad) {
     a.reset_accumulators();
     for (int s = 0, t = 0; s < p.n_seg; ++s) {
-      const int cnt = p.seg[s].count;
+      const int cnt = seg_count(p, s, a.dyn_r);
       for (int n0 = 0; n0 + A::KT <= cnt; n0 += A::KT, ++t) {
         if (t < f0 || t >= f0 + n_full) continue;
         __amdgpu_buffer_rsrc_t rk, rv;
@@ -1088,7 +1091,7 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(const AttnParams p) {
 
   for (int s = 0; s < p.n_seg; ++s) {
     const Segment sg = p.seg[s];
-    const int count = sg.count;
+    const int count = seg_count(p, s, dyn_r);
     const float* kbase = reinterpret_cast<const float*>(seg_base(p, s, true, dyn_r)) + (size_t)head * sg.head;
     const float* vbase = reinterpret_cast<const float*>(seg_base(p, s, false, dyn_r)) + (size_t)head * sg.head;
     for (int n0 = 0; n0 < count; n0 += KT) {
@@ -1139,7 +1142,7 @@ void plan_split(AttnParams& p, int n_cu) {
   const int nj = (p.n_heads + 7) / 8 * p.n_qtiles;
   const int F = nj / c, R = nj - F * c;
   int best = 1;
-  if (R > 0 && p.part != nullptr) {
+  if (R > 0 && p.part != nullptr && !p.dyn_may_vanish) {
     const double o = 0.15 + 8.0 / p.units;
     double best_cost = 1e30;
     for (int sp = 1; sp <= kMaxSplit && sp <= p.units; ++sp) {

@@ -174,12 +174,14 @@ __device__ inline double dot_f64(const double* __restrict__ a, const double* __r
   return wave_sum(acc);
 }
 
-// Fingerprint + retrieval, one wave64.
+// Fingerprint + retrieval, one wave64.  Entries fill the bank in slot order
+// (id -1 = empty).
 __global__ __launch_bounds__(64) void retrieve_kernel(const float* __restrict__ fp_raw,
                                                       double* __restrict__ phi_cur,
                                                       const double* __restrict__ bank_phi,
                                                       DevState* __restrict__ st, int fp_dim,
-                                                      int bank_count, int block, int32_t* slot_out) {
+                                                      const BankRule rule, int block,
+                                                      int32_t* slot_out) {
   const int lane = threadIdx.x;
   // phi_b = x / ||x||_2, zero stays zero
   double ss = 0.0;
@@ -193,32 +195,49 @@ __global__ __launch_bounds__(64) void retrieve_kernel(const float* __restrict__ 
     phi_cur[k] = nrm > 0.0 ? x / nrm : 0.0;
   }
   __syncthreads();  // phi_cur is re-read below by other lanes
-  // r(b) = argmax over entries whose id != b-1; strict '>' keeps the lowest slot on ties
+  // r(b) = argmax over entries whose id != b-1; strict '>' keeps the lowest
+  // slot on ties.  best: over every entry (the gated refresh's distance).
+  const bool undetected = nrm == 0.0 && (rule.policy & kBankZeroFallback);
   int r = -1;
-  double best = 0.0;
-  for (int s = 0; s < bank_count; ++s) {
+  double best_r = 0.0, best = -INFINITY;
+  for (int s = 0; s < rule.size; ++s) {
+    if (st->ids[s] < 0) continue;
     const double sc = dot_f64(phi_cur, bank_phi + (size_t)s * fp_dim, fp_dim, lane);
-    if (st->ids[s] == block - 1) continue;
-    if (r < 0 || sc > best) { r = s; best = sc; }
+    best = fmax(best, sc);
+    if (st->ids[s] == block - 1 || undetected) continue;
+    if (r < 0 || sc > best_r) { r = s; best_r = sc; }
   }
   if (lane == 0) {  // the Dynamic Sink of this block is bank entry r (none if r < 0)
     st->last_r = r;
     st->dyn_id = r >= 0 ? st->ids[r] : -1;
+    if (r >= 0) st->last_used[r] = block;
+    st->phi_zero = nrm == 0.0;
+    st->best = best;
     if (slot_out) *slot_out = r;
   }
 }
 
-// Diversity bank update, one wave64.
+// Diversity bank update, one wave64.  The fill phase (block < fill_blocks)
+// inserts while there is room and then swaps by exhaustive search; later
+// blocks update only under the CONTINUAL (stale entries may go) or GATED
+// (far fingerprint: full search) policies.  A zero fingerprint under
+// ZERO_FALLBACK is never written.
 __global__ __launch_bounds__(64) void bank_update_kernel(const double* __restrict__ phi_cur,
                                                          double* __restrict__ bank_phi,
                                                          DevState* __restrict__ st, int fp_dim,
-                                                         int bank_size, int bank_count, int block,
+                                                         const BankRule rule, int block,
                                                          int win_slot, int bank_slot0) {
   const int lane = threadIdx.x;
-  const int M = bank_size;
+  const int M = rule.size;
+  int count = 0;
+  while (count < M && st->ids[count] >= 0) ++count;
+  const bool filling = block < rule.fill_blocks;
+  const bool refresh = filling || ((rule.policy & kBankGated) && st->best < rule.refresh_tau);
   int dec;  // -1 keep, j = entry to write
-  if (bank_count < M) {
-    dec = bank_count;
+  if (st->phi_zero && (rule.policy & kBankZeroFallback)) {
+    dec = -1;
+  } else if (count < M) {
+    dec = count;
   } else {
     __shared__ double G[kMaxBank][kMaxBank];  // pairwise dots of the bank, i < j
     __shared__ double g[kMaxBank];            // dots with the candidate
@@ -240,6 +259,9 @@ __global__ __launch_bounds__(64) void bank_update_kernel(const double* __restric
     double best = tot / npairs;
     dec = -1;
     for (int x = 0; x < M; ++x) {
+      const bool evictable = refresh || ((rule.policy & kBankContinual) &&
+                                         block - st->last_used[x] >= rule.stale_blocks);
+      if (!evictable) continue;
       double t = 0.0;
       for (int i = 0; i < M; ++i)
         for (int j = i + 1; j < M; ++j) t += (i == x) ? g[j] : (j == x) ? g[i] : G[i][j];
@@ -254,6 +276,7 @@ __global__ __launch_bounds__(64) void bank_update_kernel(const double* __restric
     st->decision = dec;
     if (dec >= 0) {
       st->ids[dec] = block;
+      st->last_used[dec] = block;
       st->copy_src = win_slot;
       st->copy_dst = bank_slot0 + dec;
     } else {
@@ -264,8 +287,13 @@ __global__ __launch_bounds__(64) void bank_update_kernel(const double* __restric
 
 __global__ void state_init_kernel(DevState* st) {
   const int i = threadIdx.x;
-  if (i < kMaxBank) st->ids[i] = -1;
+  if (i < kMaxBank) {
+    st->ids[i] = -1;
+    st->last_used[i] = -1;
+  }
   if (i == 0) {
+    st->phi_zero = 0;
+    st->best = -INFINITY;
     st->last_r = -1;
     st->dyn_id = -1;
     st->decision = -2;
@@ -317,18 +345,18 @@ hipError_t launch_slot_copy(char* block_base, size_t slot_bytes, size_t copy_byt
 }
 
 hipError_t launch_retrieve(const float* fp_raw, double* phi_cur, const double* bank_phi,
-                           DevState* st, int fp_dim, int bank_count, int block, int32_t* slot_out,
+                           DevState* st, int fp_dim, const BankRule& rule, int block, int32_t* slot_out,
                            hipStream_t s) {
   hipLaunchKernelGGL(retrieve_kernel, dim3(1), dim3(64), 0, s, fp_raw, phi_cur, bank_phi, st,
-                     fp_dim, bank_count, block, slot_out);
+                     fp_dim, rule, block, slot_out);
   return hipGetLastError();
 }
 
 hipError_t launch_bank_update(const double* phi_cur, double* bank_phi, DevState* st, int fp_dim,
-                              int bank_size, int bank_count, int block, int win_slot,
-                              int bank_slot0, hipStream_t s) {
+                              const BankRule& rule, int block, int win_slot, int bank_slot0,
+                              hipStream_t s) {
   hipLaunchKernelGGL(bank_update_kernel, dim3(1), dim3(64), 0, s, phi_cur, bank_phi, st, fp_dim,
-                     bank_size, bank_count, block, win_slot, bank_slot0);
+                     rule, block, win_slot, bank_slot0);
   return hipGetLastError();
 }
 

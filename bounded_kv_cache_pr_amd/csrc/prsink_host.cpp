@@ -100,6 +100,11 @@ bool check_config(const pr_sink_config* c) {
   if (c->fp_dim < 1 || c->fp_dim > 4096) return fail(PR_SINK_EINVAL, "fp_dim must be 1..4096"), false;
   if (c->dtype != PR_SINK_BF16 && c->dtype != PR_SINK_F32) return fail(PR_SINK_EINVAL, "unknown dtype"), false;
   if (c->t0 < 0 || c->t0 > (1 << 20)) return fail(PR_SINK_EINVAL, "t0 out of range"), false;
+  if (c->bank_policy & ~7) return fail(PR_SINK_EINVAL, "unknown bank_policy bits"), false;
+  if ((c->bank_policy & PR_SINK_BANK_CONTINUAL) && c->bank_stale_blocks < 1)
+    return fail(PR_SINK_EINVAL, "bank_stale_blocks must be >= 1"), false;
+  if ((c->bank_policy & PR_SINK_BANK_GATED) && !(c->bank_refresh_tau >= -1.0 && c->bank_refresh_tau <= 1.0))
+    return fail(PR_SINK_EINVAL, "bank_refresh_tau must be in [-1, 1]"), false;
   const long long tpf = (long long)c->lat_h * c->lat_w;
   if (tpf * c->block_frames > (1 << 24) || tpf * c->ref_frames > (1 << 24)) return fail(PR_SINK_EINVAL, "block too large"), false;
   const uint32_t n_max = (uint32_t)(tpf * (c->block_frames > c->ref_frames ? c->block_frames : c->ref_frames));
@@ -317,6 +322,10 @@ void add_job(RotParams& r, const void* src, void* dst, int t_index) {
   j.from_state = 0;
 }
 
+BankRule bank_rule(const pr_sink_config& g) {
+  return BankRule{g.bank_size, g.bank_fill_blocks, g.bank_policy, g.bank_stale_blocks, g.bank_refresh_tau};
+}
+
 size_t block_bytes(const pr_sink_cache* c, int n_tok) {
   return (size_t)n_tok * c->cfg.n_heads * c->cfg.head_dim * c->lay.elem;
 }
@@ -433,9 +442,12 @@ int pr_sink_retrieve(pr_sink_cache* c, int32_t block, const float* fp_raw_dev,
   if (block != c->next_block) return fail(PR_SINK_ESTATE, "expected block %d, got %d", c->next_block, block);
   for (int l = 0; l < c->cfg.n_layers; ++l)
     if (!c->ref_set[l]) return fail(PR_SINK_ESTATE, "Ref Sink of layer %d not set", l);
-  // The host knows whether a candidate exists: the first M blocks are always
-  // inserted, so a bank with one entry holds block 0, and a fuller bank holds
-  // several distinct blocks of which at most one is block-1.
+  // The host knows whether a candidate exists: every bank update inserts while
+  // there is room, so a bank with one entry holds block 0, and a fuller bank
+  // holds several distinct blocks of which at most one is block-1.  Under
+  // ZERO_FALLBACK an undetected block is not inserted and retrieves nothing,
+  // so bank_count is an upper bound and the attention kernels drop the
+  // Dynamic segment themselves when the device found no entry.
   const bool candidate = c->bank_count >= 2 || (c->bank_count == 1 && block - 1 != 0);
   if (!c->dry) {
     const pr_sink_config& g = c->cfg;
@@ -451,7 +463,7 @@ int pr_sink_retrieve(pr_sink_cache* c, int32_t block, const float* fp_raw_dev,
     // r lands in the device state; attention reads bank entry r in place (its
     // K is kept rotated at the Dynamic Sink's place), so nothing is copied
     PRS_HIP(launch_retrieve(fp_raw_dev, c->phi_cur(), c->phi_bank(), c->state(), g.fp_dim,
-                            c->bank_count, block, slot_out_dev, s));
+                            bank_rule(g), block, slot_out_dev, s));
     // RoPE follow for the window blocks that move one place as this block
     // opens.  The previous block's keys are already at the newest window
     // place, and block 0's at the Static Sink's: clean_kv_write rotated them.
@@ -545,6 +557,7 @@ int pr_sink_attend(pr_sink_cache* c, int32_t layer, const void* q_raw, const voi
   p.n_heads = g.n_heads;
   p.q_t_index = t_index[n_seg - 1];
   p.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)g.head_dim));
+  p.dyn_may_vanish = (g.bank_policy & PR_SINK_BANK_ZERO_FALLBACK) != 0;
   p.part = L.n_part_rec ? reinterpret_cast<float*>(c->arena + L.off_part) : nullptr;
   p.cnt = L.n_cnt ? reinterpret_cast<uint32_t*>(c->arena + L.off_cnt) : nullptr;
   if (c->time_start) PRS_HIP(hipEventRecord(c->time_start, st));
@@ -602,6 +615,9 @@ int pr_sink_bank_update(pr_sink_cache* c, int32_t block, void* stream) {
     if (!c->written[l]) return fail(PR_SINK_ESTATE, "clean K/V of layer %d not written for block %d", l, block);
   const pr_sink_config& g = c->cfg;
   hipStream_t s = as_stream(stream);
+  // the bank is written during the fill phase, and later under the CONTINUAL
+  // and GATED policies (the device decides whether anything changes)
+  const bool update = block < g.bank_fill_blocks || (g.bank_policy & (PR_SINK_BANK_CONTINUAL | PR_SINK_BANK_GATED));
   if (!c->dry) {
     // every clean write of this block (the bank copies the window slot, and
     // the block's completion mark covers them), and its attention (which read
@@ -609,12 +625,12 @@ int pr_sink_bank_update(pr_sink_cache* c, int32_t block, void* stream) {
     for (auto& m : c->clean) PRS_HIP(after(s, m));
     PRS_HIP(after(s, c->attn));
   }
-  if (block < g.bank_fill_blocks) {
+  if (update) {
     if (!c->dry) {
       const Layout& L = c->lay;
       const int ws = c->bs_window(block % g.window_slots);
-      PRS_HIP(launch_bank_update(c->phi_cur(), c->phi_bank(), c->state(), g.fp_dim, g.bank_size,
-                                 c->bank_count, block, ws, c->bs_bank(0), s));
+      PRS_HIP(launch_bank_update(c->phi_cur(), c->phi_bank(), c->state(), g.fp_dim, bank_rule(g), block,
+                                 ws, c->bs_bank(0), s));
       // the written entry gets the block's raw K and V, and its K rotated at
       // the Dynamic Sink's place, the only place a bank entry is attended from
       PRS_HIP(launch_slot_copy(c->block_slot(0), L.slot_b, 2 * L.kv_b * g.n_layers, c->state(), s));

@@ -10,6 +10,8 @@ namespace prsink {
 
 constexpr int kMaxSegments = 8;   // Ref, Static, Dynamic, <= 4 previous window blocks, current
 constexpr int kMaxBank = 8;
+// Bank-policy bits, the values of pr_sink_bank_policy.
+constexpr int kBankZeroFallback = 1, kBankContinual = 2, kBankGated = 4;
 constexpr int kKeyTile = 64;      // keys per attention tile; slot token counts pad to this
 constexpr int kMaxRotJobs = 6;    // rotation jobs per rope_follow launch
 
@@ -98,24 +100,34 @@ struct AttnParams {
   const char* dyn_v0;
   int64_t dyn_stride;
   int32_t dyn_seg;
+  // the device may find no entry although the host planned a Dynamic segment
+  // (an undetected pose under the zero-fingerprint fallback): the segment then
+  // counts 0 keys, and the work is not split
+  int32_t dyn_may_vanish;
 };
 
 // The bank entry the Dynamic Sink reads, loaded once per workgroup with a
 // scalar load (the value then stays in SGPRs, so addresses built from it can
-// feed buffer resources; the load waits for itself inside the asm).  0 when
-// the block has no Dynamic Sink or no entry was found.
+// feed buffer resources; the load waits for itself inside the asm).  -1 when
+// the device found no entry; 0 when the block has no Dynamic segment.
 __device__ inline int load_dyn_r(const AttnParams& p) {
   if (p.dyn_seg < 0) return 0;
   int r;
   asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(r) : "s"(p.dyn_r) : "memory");
-  return r > 0 ? r : 0;
+  return r;
+}
+
+// Keys of segment s: the Dynamic segment is empty when no entry was found.
+__device__ inline int seg_count(const AttnParams& p, int s, int dyn_r) {
+  const int c = p.seg[s].count;
+  return s == p.dyn_seg && dyn_r < 0 ? 0 : c;
 }
 
 // K (is_k) or V base of segment s; dyn_r from load_dyn_r.  Written as a
 // select of two computed bases: an early return here let the compiler treat
 // the result as divergent and move it to VGPRs.
 __device__ inline const char* seg_base(const AttnParams& p, int s, bool is_k, int dyn_r) {
-  const char* dyn = (is_k ? p.dyn_k0 : p.dyn_v0) + (int64_t)dyn_r * p.dyn_stride;
+  const char* dyn = (is_k ? p.dyn_k0 : p.dyn_v0) + (int64_t)(dyn_r > 0 ? dyn_r : 0) * p.dyn_stride;
   const char* seg = static_cast<const char*>(is_k ? p.seg[s].k : p.seg[s].v);
   return s == p.dyn_seg ? dyn : seg;
 }
@@ -135,7 +147,9 @@ struct DevState {
   int32_t decision;        // last bank decision: -2 none, -1 keep, j = entry written
   int32_t copy_src;        // pending slot copy: source block-slot index, -1 = skip
   int32_t copy_dst;        // destination block-slot index
-  int32_t pad_[3];
+  int32_t last_used[kMaxBank];  // block at which each entry was last written or retrieved
+  int32_t phi_zero;        // the open block's fingerprint is all zero
+  double best;             // the open block's best dot product with the bank (-inf: empty bank)
 };
 
 // One RoPE-follow job: rotate raw keys [n_tok][H][d] of n_layers layers at the
@@ -184,11 +198,16 @@ hipError_t launch_kv_write(const void* k_src, const void* v_src, void* k_dst0, v
 hipError_t launch_clean_write(const CleanWrite& p, hipStream_t s);
 hipError_t launch_slot_copy(char* block_base, size_t slot_bytes, size_t copy_bytes,
                             const DevState* st, hipStream_t s);
+// Bank update rules of one cache (pr_sink_config's bank fields).
+struct BankRule {
+  int32_t size, fill_blocks, policy, stale_blocks;
+  double refresh_tau;
+};
 hipError_t launch_retrieve(const float* fp_raw, double* phi_cur, const double* bank_phi,
-                           DevState* st, int fp_dim, int bank_count, int block,
+                           DevState* st, int fp_dim, const BankRule& rule, int block,
                            int32_t* slot_out, hipStream_t s);
 hipError_t launch_bank_update(const double* phi_cur, double* bank_phi, DevState* st,
-                              int fp_dim, int bank_size, int bank_count, int block,
+                              int fp_dim, const BankRule& rule, int block,
                               int win_slot, int bank_slot0, hipStream_t s);
 hipError_t launch_state_init(DevState* st, hipStream_t s);
 

@@ -99,7 +99,35 @@ typedef struct pr_sink_config {
   int32_t fp_dim;           /* pose fingerprint length, 1..4096                      */
   int32_t dtype;            /* pr_sink_dtype of K/V/Q/out                            */
   int32_t t0;               /* temporal position of the first Ref frame, >= 0        */
+  /* Bank-policy variants (review, weaknesses paragraph: directions for the
+   * frozen bank and for failed pose detection), bits of pr_sink_bank_policy;
+   * 0 = the method as described. */
+  int32_t bank_policy;
+  int32_t bank_stale_blocks; /* CONTINUAL: blocks an entry must go unused before it
+                                may be evicted (its weight halves every this many
+                                blocks, eviction at weight 1/2), >= 1              */
+  double bank_refresh_tau;   /* GATED: refresh when the best dot product of the block's
+                                fingerprint with the bank is below this, in [-1, 1] */
 } pr_sink_config;
+
+/* Bank-policy bits (pr_sink_config.bank_policy).
+ *   ZERO_FALLBACK  a block whose fingerprint is all zero (every frame failed
+ *                  detection) attends no Dynamic Sink (Static Sink + window
+ *                  only) and is never written into the bank.
+ *   CONTINUAL      past the fill phase the exhaustive replacement keeps
+ *                  running, restricted to entries not written or retrieved in
+ *                  the last bank_stale_blocks blocks (continual writes with
+ *                  decaying weights).
+ *   GATED          past the fill phase, a block whose best dot product with
+ *                  the bank is below bank_refresh_tau triggers the full
+ *                  exhaustive replacement (refresh gated by fingerprint
+ *                  distance).
+ * While the bank has room, any update inserts into the next slot. */
+typedef enum {
+  PR_SINK_BANK_ZERO_FALLBACK = 1,
+  PR_SINK_BANK_CONTINUAL = 2,
+  PR_SINK_BANK_GATED = 4
+} pr_sink_bank_policy;
 
 typedef struct pr_sink_cache pr_sink_cache; /* opaque, host-side handle */
 

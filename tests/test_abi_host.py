@@ -65,6 +65,8 @@ def test_arena_bytes_closed_form():
     dict(n_layers=0), dict(window_slots=0), dict(window_slots=6), dict(bank_size=1),
     dict(bank_size=9), dict(fp_dim=0), dict(rope_theta=0.0), dict(lat_h=0), dict(t0=-1),
     dict(block_frames=0), dict(bank_fill_blocks=-1),
+    dict(bank_policy=8), dict(bank_policy=2, bank_stale_blocks=0),
+    dict(bank_policy=4, bank_refresh_tau=1.5), dict(bank_policy=4, bank_refresh_tau=float("nan")),
 ])
 def test_invalid_configs_are_rejected(bad):
     cfg = synth.C1_480.replace(**bad)
