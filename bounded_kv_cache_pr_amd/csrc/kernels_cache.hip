@@ -1,7 +1,7 @@
 // Cache-maintenance kernels of the PR-Sink path on gfx950:
 //   kv_write     raw K/V [T][H][d] -> slot layout [t_pad][H][d] (contiguous copy)
 //   clean_write  the same for a closing block's clean K/V, plus its keys
-//                rotated at the place they take next
+//                rotated at every window place they will take
 //   rope_follow  raw keys -> keys rotated at a segment's current positions
 //   slot_copy    the first bytes of a block slot (all layers) -> another slot;
 //                source and destination come from device state, so no host
@@ -126,10 +126,11 @@ __global__ __launch_bounds__(256) void rope_follow_kernel(const RotParams p) {
 
 // ---------------------------------------------------------------------------
 // clean_write: the clean K/V of one layer of the block being closed go to its
-// window slot, raw, together with the keys rotated at the place the block
-// takes when the next block opens (the newest window place); for block 0 the
-// same three tensors also go to the Static Sink, rotated at its place.  One
-// pass reads the clean keys once.  Thread = one 16-byte chunk of K and of V.
+// window slot, raw, together with its keys rotated at every window place the
+// block takes while it stays in the window (newest first); for block 0 the
+// raw tensors also go to the Static Sink, with the keys rotated at its place.
+// One pass reads the clean keys once, and no key is rotated again when the
+// window slides.  Thread = one 16-byte chunk of K and of V.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void clean_write_kernel(const CleanWrite p) {
   const uint32_t per_head = (uint32_t)(p.head_dim * p.elem / 16);
@@ -148,10 +149,12 @@ __global__ __launch_bounds__(256) void clean_write_kernel(const CleanWrite p) {
       if (!o.k) continue;
       reinterpret_cast<uint4*>(o.k)[i] = k;
       reinterpret_cast<uint4*>(o.v)[i] = v;
-      if (o.k_rot) {
+#pragma unroll
+      for (int r = 0; r < kMaxRot; ++r) {
+        if (r >= o.n_rot) break;
         int tt, y, x;
-        token_pos(p.g, (int)n, o.t_index, tt, y, x);
-        reinterpret_cast<uint4*>(o.k_rot)[i] = rotate_chunk(p.g, k, c, p.elem, tt, y, x);
+        token_pos(p.g, (int)n, o.t_index[r], tt, y, x);
+        reinterpret_cast<uint4*>(o.k_rot[r])[i] = rotate_chunk(p.g, k, c, p.elem, tt, y, x);
       }
     }
   }

@@ -74,7 +74,8 @@ struct Layout {
   size_t kv_b, slot_b;   // block slot: one tensor of one layer, whole slot
   size_t kv_r, slot_r;   // Ref slot
   size_t off_state, off_phi_bank, off_phi_cur, off_rope, off_cur_rot, off_part, off_cnt, off_ref, off_blocks,
-      total;
+      off_wrot, total;
+  size_t wrot_b;             // per window slot: its keys rotated at the older window places
   size_t n_part_rec, n_cnt;  // partial records and counters of split attention jobs
   int n_t, np_t, np_h, np_w, rope_h_off, rope_w_off, rope_entries;
   int n_block_slots;
@@ -166,6 +167,11 @@ Layout make_layout(const pr_sink_config* c) {
   off += L.slot_r;
   L.off_blocks = off;
   off += L.slot_b * L.n_block_slots;
+  // a window block is attended at W-1 places; the block slot holds its keys
+  // rotated at the newest one, this area the W-2 older ones
+  L.off_wrot = off;
+  L.wrot_b = c->window_slots >= 3 ? align_up((size_t)(c->window_slots - 2) * L.kv_b * c->n_layers, kAlign) : 0;
+  off += L.wrot_b * c->window_slots;
   L.total = off;
   return L;
 }
@@ -215,19 +221,22 @@ struct pr_sink_cache {
     hipEvent_t ev = nullptr;
     hipStream_t st = nullptr;
     bool set = false;
+    bool waited = false;          // `seen` already waits for this recording
+    hipStream_t seen = nullptr;   // (the null stream is a stream too)
   };
   std::vector<Mark> clean;  // per layer: the last clean write of that layer
   Mark ref;                 // the last Ref Sink write
   Mark attn;                // the last attention call
   Mark retr;                // the last retrieval
-  Mark bank;                // the last bank update that wrote the bank
-  Mark done[2];             // block b's clean writes all complete, at [b & 1]
+  Mark dec;                 // the last bank decision (state only; entries may still be copying)
+  Mark bank;                // the last bank update that wrote the bank, its copies included
+  Mark done[2];             // block b's bank update complete, at [b & 1]
   hipEvent_t time_start = nullptr, time_stop = nullptr;  // caller's events around the attention kernel
 
   ~pr_sink_cache() {
     auto drop = [](Mark& m) { if (m.ev) (void)hipEventDestroy(m.ev); };
     for (Mark& m : clean) drop(m);
-    drop(ref); drop(attn); drop(retr); drop(bank); drop(done[0]); drop(done[1]);
+    drop(ref); drop(attn); drop(retr); drop(dec); drop(bank); drop(done[0]); drop(done[1]);
   }
 
   char* block_slot(int bs) const { return arena + lay.off_blocks + (size_t)bs * lay.slot_b; }
@@ -241,6 +250,14 @@ struct pr_sink_cache {
   double* phi_cur() const { return reinterpret_cast<double*>(arena + lay.off_phi_cur); }
   const float2* rope() const { return reinterpret_cast<const float2*>(arena + lay.off_rope); }
   int bs_static() const { return 0; }
+  // Keys of window slot j rotated at window place p (0 = oldest, W-2 = newest)
+  // for layer l.
+  char* window_rot(int j, int p, int l) const {
+    if (p == cfg.window_slots - 2) return block_slot(bs_window(j)) + r_off(l, lay.kv_b);
+    return arena + lay.off_wrot + (size_t)j * lay.wrot_b + ((size_t)p * cfg.n_layers + l) * lay.kv_b;
+  }
+  // First temporal row of window place p.
+  int window_t(int p) const { return cfg.ref_frames + (2 + p) * cfg.block_frames; }
   int bs_window(int j) const { return 1 + j; }
   int bs_bank(int i) const { return 1 + cfg.window_slots + i; }
 };
@@ -330,15 +347,24 @@ size_t block_bytes(const pr_sink_cache* c, int n_tok) {
   return (size_t)n_tok * c->cfg.n_heads * c->cfg.head_dim * c->lay.elem;
 }
 
-// Stream s waits for producer m if m ran on another stream.
-hipError_t after(hipStream_t s, const pr_sink_cache::Mark& m) {
-  if (!m.set || m.st == s) return hipSuccess;
-  return hipStreamWaitEvent(s, m.ev, 0);
+// Stream s waits for producer m if m ran on another stream and s has not
+// waited for this recording of m yet (a stream wait is a queue packet that
+// costs microseconds between kernels; the three denoise steps of a layer
+// would otherwise each wait for the same clean write).
+hipError_t after(hipStream_t s, pr_sink_cache::Mark& m) {
+  if (!m.set || m.st == s || (m.waited && m.seen == s)) return hipSuccess;
+  const hipError_t e = hipStreamWaitEvent(s, m.ev, 0);
+  if (e == hipSuccess) {
+    m.waited = true;
+    m.seen = s;
+  }
+  return e;
 }
 // Marks the work queued so far on s as producer m.
 hipError_t mark(hipStream_t s, pr_sink_cache::Mark& m) {
   m.st = s;
   m.set = true;
+  m.waited = false;
   return hipEventRecord(m.ev, s);
 }
 
@@ -396,7 +422,7 @@ int pr_sink_cache_init(const pr_sink_config* cfg, void* arena_dev, size_t arena_
     auto make = [](pr_sink_cache::Mark& m) { return hipEventCreateWithFlags(&m.ev, hipEventDisableTiming); };
     hipError_t e = hipSuccess;
     for (auto& m : c->clean) if (e == hipSuccess) e = make(m);
-    for (auto* m : {&c->ref, &c->attn, &c->retr, &c->bank, &c->done[0], &c->done[1]})
+    for (auto* m : {&c->ref, &c->attn, &c->retr, &c->dec, &c->bank, &c->done[0], &c->done[1]})
       if (e == hipSuccess) e = make(*m);
     if (e != hipSuccess) {
       delete c;
@@ -451,30 +477,22 @@ int pr_sink_retrieve(pr_sink_cache* c, int32_t block, const float* fp_raw_dev,
   const bool candidate = c->bank_count >= 2 || (c->bank_count == 1 && block - 1 != 0);
   if (!c->dry) {
     const pr_sink_config& g = c->cfg;
-    const Layout& L = c->lay;
     hipStream_t s = as_stream(stream);
-    // the bank state and entries of the last bank update; the raw keys of the
-    // window blocks that move (block-2 and older, written by the time block-2
-    // closed); the previous block's attention, which read the state and the
-    // rotated keys rewritten here
-    PRS_HIP(after(s, c->bank));
+    // the bank state of the last bank decision: not its entry copy, since the
+    // entry it writes holds block-1, which this retrieval excludes (the other
+    // entries were written by block-2's update at the latest); the whole update
+    // of block-2 (entries this block may retrieve); the previous block's
+    // attention, which read the state
+    PRS_HIP(after(s, c->dec));
     if (block >= 2) PRS_HIP(after(s, c->done[block & 1]));
     PRS_HIP(after(s, c->attn));
     // r lands in the device state; attention reads bank entry r in place (its
-    // K is kept rotated at the Dynamic Sink's place), so nothing is copied
+    // K is kept rotated at the Dynamic Sink's place), so nothing is copied.
+    // Nothing is rotated either: the window blocks' keys were rotated at every
+    // window place when they were written, block 0's also at the Static
+    // Sink's.
     PRS_HIP(launch_retrieve(fp_raw_dev, c->phi_cur(), c->phi_bank(), c->state(), g.fp_dim,
                             bank_rule(g), block, slot_out_dev, s));
-    // RoPE follow for the window blocks that move one place as this block
-    // opens.  The previous block's keys are already at the newest window
-    // place, and block 0's at the Static Sink's: clean_kv_write rotated them.
-    RotParams r = rot_params(c, L.tb, L.kv_b);
-    for (int j = 0; j < g.window_slots - 2; ++j) {
-      const int id = block - (g.window_slots - 1) + j;
-      if (id < 0) continue;
-      char* w = c->block_slot(c->bs_window(id % g.window_slots));
-      add_job(r, w + c->k_off(0, L.kv_b), w + c->r_off(0, L.kv_b), g.ref_frames + (2 + j) * g.block_frames);
-    }
-    if (r.n_jobs) PRS_HIP(launch_rope_follow(r, g.n_layers, s));
     PRS_HIP(mark(s, c->retr));
   }
   c->dyn_present = candidate;
@@ -538,15 +556,14 @@ int pr_sink_attend(pr_sink_cache* c, int32_t layer, const void* q_raw, const voi
         p.dyn_v0 = c->block_slot(c->bs_bank(0)) + c->v_off(layer, L.kv_b);
         p.dyn_stride = (int64_t)L.slot_b;
       }
-    } else {
-      int bs;
-      if (s == 1) bs = c->bs_static();
-      else {
-        const int id = b - (g.window_slots - 1) + (s - 3);
-        bs = c->bs_window(id >= 0 ? id % g.window_slots : 0);
-      }
-      sg.k = c->block_slot(bs) + c->r_off(layer, L.kv_b);
-      sg.v = c->block_slot(bs) + c->v_off(layer, L.kv_b);
+    } else if (s == 1) {  // Static Sink
+      sg.k = c->block_slot(c->bs_static()) + c->r_off(layer, L.kv_b);
+      sg.v = c->block_slot(c->bs_static()) + c->v_off(layer, L.kv_b);
+    } else {  // window place s - 3: block b - (W-1) + (s-3)
+      const int id = b - (g.window_slots - 1) + (s - 3);
+      const int j = id >= 0 ? id % g.window_slots : 0;
+      sg.k = c->window_rot(j, s - 3, layer);
+      sg.v = c->block_slot(c->bs_window(j)) + c->v_off(layer, L.kv_b);
     }
   }
   p.q = q_raw;
@@ -587,20 +604,32 @@ int pr_sink_clean_kv_write(pr_sink_cache* c, int32_t layer, const void* k_raw, c
     cw.n_heads = g.n_heads;
     cw.head_dim = g.head_dim;
     cw.elem = L.elem;
-    // the window slot, with the keys rotated at the newest window place, the
-    // one this block takes when the next block opens (no window place to
-    // take when the window holds only the current block)
-    cw.dst[0] = {w + c->k_off(layer, L.kv_b), w + c->v_off(layer, L.kv_b),
-                 g.window_slots >= 2 ? w + c->r_off(layer, L.kv_b) : nullptr,
-                 g.ref_frames + g.window_slots * g.block_frames};
+    // the window slot, with the keys rotated at each window place the block
+    // takes from the next block on, newest first (none when the window holds
+    // only the current block)
+    const int j = b % g.window_slots;
+    cw.dst[0].k = w + c->k_off(layer, L.kv_b);
+    cw.dst[0].v = w + c->v_off(layer, L.kv_b);
+    for (int p = g.window_slots - 2; p >= 0; --p) {
+      CleanDst& d = cw.dst[0];
+      d.k_rot[d.n_rot] = c->window_rot(j, p, layer);
+      d.t_index[d.n_rot++] = c->window_t(p);
+    }
     if (b == 0) {  // block 0 is also the Static Sink, from block 1 on
       char* st = c->block_slot(c->bs_static());
-      cw.dst[1] = {st + c->k_off(layer, L.kv_b), st + c->v_off(layer, L.kv_b), st + c->r_off(layer, L.kv_b),
-                   g.ref_frames};
+      CleanDst& d = cw.dst[1];
+      d.k = st + c->k_off(layer, L.kv_b);
+      d.v = st + c->v_off(layer, L.kv_b);
+      d.k_rot[0] = st + c->r_off(layer, L.kv_b);
+      d.t_index[0] = g.ref_frames;
+      d.n_rot = 1;
     }
-    // the window slot last held block b-W, which the previous block attended
+    // the window slot last held block b-W: its last reader was the previous
+    // block's attention, and its bank copy (block b-W's update) came before
+    // that; this block's retrieval waited for both, and this block's own
+    // attention reads other slots, so the write may overlap it
     hipStream_t s = as_stream(stream);
-    PRS_HIP(after(s, c->attn));
+    PRS_HIP(after(s, c->retr));
     PRS_HIP(launch_clean_write(cw, s));
     PRS_HIP(mark(s, c->clean[layer]));
   }
@@ -619,18 +648,30 @@ int pr_sink_bank_update(pr_sink_cache* c, int32_t block, void* stream) {
   // and GATED policies (the device decides whether anything changes)
   const bool update = block < g.bank_fill_blocks || (g.bank_policy & (PR_SINK_BANK_CONTINUAL | PR_SINK_BANK_GATED));
   if (!c->dry) {
-    // every clean write of this block (the bank copies the window slot, and
-    // the block's completion mark covers them), and its attention (which read
-    // bank entries as the Dynamic Sink)
-    for (auto& m : c->clean) PRS_HIP(after(s, m));
+    // this block's retrieval (it wrote the fingerprint and the scores the
+    // decision reads) and attention (it read bank entries as the Dynamic
+    // Sink), and the previous update's copies (they read the copy plan the
+    // decision below rewrites)
+    PRS_HIP(after(s, c->retr));
     PRS_HIP(after(s, c->attn));
+    PRS_HIP(after(s, c->bank));
   }
+  // every clean write of this block: the bank copies the window slot, and the
+  // block's completion mark covers them
+  auto after_clean = [&]() -> hipError_t {
+    for (auto& m : c->clean)
+      if (hipError_t e = after(s, m)) return e;
+    return hipSuccess;
+  };
   if (update) {
     if (!c->dry) {
       const Layout& L = c->lay;
       const int ws = c->bs_window(block % g.window_slots);
       PRS_HIP(launch_bank_update(c->phi_cur(), c->phi_bank(), c->state(), g.fp_dim, bank_rule(g), block,
                                  ws, c->bs_bank(0), s));
+      // the next retrieval needs the decision only (see pr_sink_retrieve)
+      PRS_HIP(mark(s, c->dec));
+      PRS_HIP(after_clean());
       // the written entry gets the block's raw K and V, and its K rotated at
       // the Dynamic Sink's place, the only place a bank entry is attended from
       PRS_HIP(launch_slot_copy(c->block_slot(0), L.slot_b, 2 * L.kv_b * g.n_layers, c->state(), s));
@@ -643,7 +684,10 @@ int pr_sink_bank_update(pr_sink_cache* c, int32_t block, void* stream) {
     }
     if (c->bank_count < g.bank_size) ++c->bank_count;
   }
-  if (!c->dry) PRS_HIP(mark(s, c->done[block & 1]));
+  if (!c->dry) {
+    PRS_HIP(after_clean());
+    PRS_HIP(mark(s, c->done[block & 1]));
+  }
   c->open = false;
   c->next_block = block + 1;
   return PR_SINK_OK;
@@ -697,6 +741,15 @@ int pr_sink_slot_view(const pr_sink_cache* c, int32_t slot, int32_t layer, void*
   *k_dev = base + c->k_off(layer, kv);
   *v_dev = base + c->v_off(layer, kv);
   if (k_rot_dev) *k_rot_dev = base + c->r_off(layer, kv);
+  const int W = c->cfg.window_slots;
+  if (k_rot_dev && W >= 2 && slot >= PR_SINK_SLOT_WINDOW0 && slot < PR_SINK_SLOT_WINDOW0 + W) {
+    // the copy at the place the slot's block holds in the window of the open
+    // (else the next) block b: block b-W+d sits at place d-1; d = 0 is the
+    // block written in block b, or the one that left the window (newest place)
+    const int j = slot - PR_SINK_SLOT_WINDOW0, b = c->next_block;
+    const int d = ((j - b) % W + W) % W;
+    *k_rot_dev = c->window_rot(j, d == 0 ? W - 2 : d - 1, layer);
+  }
   return PR_SINK_OK;
 }
 

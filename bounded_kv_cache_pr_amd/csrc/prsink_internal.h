@@ -172,14 +172,19 @@ struct RotParams {
   int32_t n_jobs, n_tok, n_heads, head_dim, elem;
 };
 
-// One destination of a clean write: raw K, V and (k_rot != nullptr) K rotated
-// at the place whose first frame has temporal row t_index.  k == nullptr:
-// unused.
+// Places a window block is attended at: one per previous-block slot of the
+// window (at most kMaxSegments - 4 of them).
+constexpr int kMaxRot = kMaxSegments - 4;
+
+// One destination of a clean write: raw K, V and n_rot copies of K, copy i
+// rotated at the place whose first frame has temporal row t_index[i].
+// k == nullptr: unused.
 struct CleanDst {
   char* k;
   char* v;
-  char* k_rot;
-  int32_t t_index;
+  char* k_rot[kMaxRot];
+  int32_t t_index[kMaxRot];
+  int32_t n_rot;
 };
 struct CleanWrite {
   const char* k_src;    // clean K of one layer, [n_tok][H][d]

@@ -21,11 +21,13 @@
  * Dynamic, the previous window blocks (oldest first) and the current block,
  * each block_frames frames long; spatial positions are the latent (row,
  * column).  An empty segment is skipped and the others keep their positions.
- * The library rotates a block's raw keys whenever the block takes a new place
- * (Ref at set-up, Static when block 1 opens, each window block as the window
- * slides, a bank entry at the Dynamic place when written, the current block on
- * every attention call) and keeps the rotated copy next to the raw keys, so a
- * key is rotated once per place rather than once per query tile.
+ * The library rotates a block's raw keys once for every place the block takes
+ * (Ref at set-up; block 0 at the Static place and a window block at each of
+ * the W-1 window places it will take, all when its clean K/V are written; a
+ * bank entry at the Dynamic place when written; the current block on every
+ * attention call) and keeps the rotated copies next to the raw keys, so a key
+ * is rotated once per place rather than once per query tile, and nothing is
+ * rotated when the window slides.
  *
  * Memory: the caller allocates ONE device arena of pr_sink_arena_bytes(cfg)
  * bytes and every input/output tensor.  The library never allocates or frees
@@ -45,11 +47,14 @@
  * another stream that it depends on), so results do not depend on the
  * streams chosen.  The intended split (review, discussion of the Clean KV
  * Update's 24 % share: overlap it) puts pr_sink_clean_kv_write and
- * pr_sink_bank_update on a second stream: block b+1's attention of layer l
- * then waits only for block b's clean write of layer l, and from the frozen
- * bank on (block >= bank_fill_blocks) retrieval waits for no clean write of
- * the block just closed.  The calls themselves must come from one host
- * thread, in the block order below.
+ * pr_sink_bank_update on a second stream.  A clean write of block b waits
+ * only for block b's retrieval (it fills the slot of block b-W, which block
+ * b's attention does not read), so it may overlap block b's attention; block
+ * b+1's attention of layer l waits for block b's clean write of layer l; the
+ * retrieval of block b+1 waits for block b's bank decision but not for the
+ * copy of the entry it writes (that entry holds block b, which the retrieval
+ * excludes), so the copy overlaps block b+1's attention.  The calls
+ * themselves must come from one host thread, in the block order below.
  *
  * Call order per block b = 0, 1, 2, ...:
  *   pr_sink_retrieve(b)  ->  pr_sink_attend(layer) any number of times
@@ -174,8 +179,8 @@ int pr_sink_set_ref(pr_sink_cache* c, int32_t layer, const void* k_raw, const vo
  * device (the host never waits for the retrieval).  The entry cannot change
  * while the block is open: the bank is written only by pr_sink_bank_update.
  * If no entry is eligible the Dynamic Sink is not attended during this block.
- * Also re-rotates the keys of the window blocks that move one place as the
- * block opens (the previous block's keys were rotated by its clean write).
+ * No key is rotated here: every window block's keys were rotated at all its
+ * window places by its clean write.
  * slot_out_dev (device int32, nullable) receives the bank slot or -1. */
 int pr_sink_retrieve(pr_sink_cache* c, int32_t block, const float* fp_raw_dev,
                      int32_t* slot_out_dev, void* stream);
@@ -195,10 +200,9 @@ int pr_sink_attend(pr_sink_cache* c, int32_t layer, const void* q_raw, const voi
  * `layer` (device, [T][H][d]) into its rolling-window slot, and for block 0
  * also into the Static Sink (review, full-pipeline paragraph; HF abstract:
  * Static Sink = first generated block).  In the same pass it stores the keys
- * rotated at the place the block takes when the next block opens (the newest
- * window place; block 0 also at the Static Sink's place), so that opening
- * the next block re-rotates only the window blocks that move again.  Once
- * per layer per block. */
+ * rotated at each of the W-1 window places the block takes from the next
+ * block on (block 0 also at the Static Sink's place), so that opening a
+ * block rotates nothing.  Once per layer per block. */
 int pr_sink_clean_kv_write(pr_sink_cache* c, int32_t layer, const void* k_raw,
                            const void* v_raw, void* stream);
 
@@ -222,9 +226,11 @@ int pr_sink_bank_state(pr_sink_cache* c, int32_t* ids_host, double* fp_host,
 /* Device pointers to the raw K, the V and the rotated K of one slot and
  * layer, for inspection.  All are [t_pad][H][d], token-major like the tensors
  * passed in; t_pad (a multiple of 64; the padding rows are zero) goes to
- * *t_pad_out.  The rotated K holds the keys rotated at the slot's place as of
- * the last block opened (a bank entry: at the Dynamic Sink's place); k_rot_dev
- * may be NULL.  PR_SINK_SLOT_DYNAMIC is rejected (PR_SINK_EINVAL): view the
+ * *t_pad_out.  The rotated K holds the keys rotated at the place the slot's
+ * block takes in the window of the open block (of the next one between
+ * blocks); for the block written in it, or one that has left the window, the
+ * newest window place.  Static: at the Static Sink's place; a bank entry: at
+ * the Dynamic Sink's place.  k_rot_dev may be NULL.  PR_SINK_SLOT_DYNAMIC is rejected (PR_SINK_EINVAL): view the
  * bank entry the open block retrieved instead. */
 int pr_sink_slot_view(const pr_sink_cache* c, int32_t slot, int32_t layer, void** k_dev,
                       void** v_dev, void** k_rot_dev, int32_t* t_pad_out);

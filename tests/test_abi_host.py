@@ -42,9 +42,11 @@ def test_arena_bytes_closed_form():
         pad = lambda n: -(-n // 64) * 64
         slots = 1 + cfg.window_slots + cfg.bank_size  # Static, window, bank (Dynamic reads a bank entry)
         row = cfg.n_heads * cfg.head_dim * esz
-        # every slot holds raw K, V and rotated K per layer; plus the current
-        # block's rotated K
+        # every slot holds raw K, V and rotated K per layer; a window block is
+        # attended at W-1 places, so each window slot keeps W-2 more rotated
+        # copies; plus the current block's rotated K
         kv = 3 * cfg.n_layers * row * (pad(cfg.ref_tokens) + slots * pad(cfg.block_tokens))
+        kv += cfg.window_slots * max(0, cfg.window_slots - 2) * cfg.n_layers * row * pad(cfg.block_tokens)
         kv += row * pad(cfg.block_tokens)
         if cfg.dtype == synth.DTYPE_BF16:
             # split attention jobs: up to 4 pieces of each of up to 32 jobs per
@@ -52,7 +54,7 @@ def test_arena_bytes_closed_form():
             # O, plus (m, l) per lane), and one counter per split job
             kv += 8 * 32 * 4 * (256 * cfg.head_dim + 1024) * 4 + 8 * 32 * 4
         n = binding.arena_bytes(cfg)
-        slack = (slots + 3) * 4096 + 3 * cfg.n_layers * (slots + 1) * 256 + (1 << 20)
+        slack = (slots + 3 + cfg.window_slots) * 4096 + 4 * cfg.n_layers * (slots + 1) * 256 + (1 << 20)
         assert kv <= n <= kv + slack
     # the footprint is a function of the config alone: it grows with layers, not with blocks
     a1 = binding.arena_bytes(synth.C1_480.replace(n_layers=1))

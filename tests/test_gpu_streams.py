@@ -204,15 +204,28 @@ def _clean_path_stream(cfg, fps, two_streams, full_blocks):
     return torch.stack(sums).cpu(), kept, (ids, phi, misc), slots
 
 
-def test_clean_path_on_second_stream_matches_one_stream():
+@pytest.mark.parametrize("policy", [0, 7])
+def test_clean_path_on_second_stream_matches_one_stream(policy):
     """Clean writes and bank updates on a second stream, ordered by the
-    library's events: the next block's attention of layer l waits only for
-    that layer's clean write.  Everything equals a one-stream run bit for
-    bit, across the bank freeze (block 20) and the window ring."""
+    library's events: a clean write waits only for its block's retrieval (it
+    overlaps that block's attention), the next block's attention of layer l
+    waits only for that layer's clean write, and the next retrieval waits
+    for the bank decision but not for the copy of the new entry.  Everything
+    equals a one-stream run bit for bit, across the bank freeze and the
+    window ring; policy 7 (zero fallback, continual writes with K = 3, gated
+    refresh) rewrites the bank every block, evicting entries that were
+    retrieved the block before."""
     cfg = synth.PRSinkConfig(n_layers=4, n_heads=8, head_dim=128, rope_dims=(44, 42, 42),
                              rope_theta=1e4, lat_h=16, lat_w=16, ref_frames=1, block_frames=3)
-    log("case: clean path on a second stream, 26 blocks, T=768, H=8")
-    fps = synth.pose_stream(26, n_protos=8, seed=6)
+    if policy:
+        cfg = cfg.replace(bank_policy=policy, bank_stale_blocks=3, bank_refresh_tau=0.85,
+                          bank_fill_blocks=8)
+        fps = np.concatenate([synth.pose_stream(13, n_protos=6, seed=5),
+                              synth.pose_stream(13, n_protos=6, seed=77)])
+        fps[[3, 15, 16]] = 0.0
+    else:
+        fps = synth.pose_stream(26, n_protos=8, seed=6)
+    log(f"case: clean path on a second stream, bank policy {policy}, 26 blocks, T=768, H=8")
     full = {1, 2, 19, 20, 21, 25}
     a = _clean_path_stream(cfg, fps, False, full)
     b = _clean_path_stream(cfg, fps, True, full)
