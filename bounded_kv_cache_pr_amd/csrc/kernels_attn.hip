@@ -145,18 +145,15 @@ __device__ __forceinline__ void dma16_run(__amdgpu_buffer_rsrc_t r, uint32_t bas
   if (restore) asm volatile("s_mov_b32 m0, %0" : : "s"(saved));
 }
 
-// The same with a per-lane 64-bit global address (a gather).
-__device__ __forceinline__ void dma16_flat(const void* gaddr, uint32_t lds) {
-  uint32_t saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %1\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %2, off\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "s"(lds), "v"(gaddr)
-      : "memory");
+// The same load as a compiler builtin, and its per-lane-address form (a
+// gather), for the prologue and the packed tiles: the compiler sets M0, keeps
+// the wait state after it, and counts the loads in its own vmcnt bookkeeping.
+__device__ __forceinline__ void dma16_b(__amdgpu_buffer_rsrc_t r, uint32_t lds, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(uintptr_t)lds, 16, voff,
+                                           soff, 0, 0);
+}
+__device__ __forceinline__ void dma16_flat_b(const void* gaddr, uint32_t lds) {
+  __builtin_amdgcn_global_load_lds(gaddr, (__attribute__((address_space(3))) void*)(uintptr_t)lds, 16, 0, 0);
 }
 
 // s_waitcnt vmcnt(n), other counters untouched (gfx9 encoding).
@@ -347,23 +344,40 @@ struct Attn {
   // This wave's share of packed tile pt into kdst / vdst: a gather, one
   // 16-byte global load per lane (rows past R repeat packed key 0 and are
   // masked later; row padding loads the row's first 16 bytes, never read).
+  // Lane L first finds the global rows of LDS row L of both tiles (K row L
+  // holds packed key key_perm(L), V row L packed key L); each DMA lane then
+  // takes the address of its row from that lane, so the segment search runs
+  // twice per lane instead of twice per DMA instruction.
   __device__ __forceinline__ void dma_packed(int pt, int R, char* kdst, char* vdst) const {
+    int kk = KT * pt + key_perm(lane), kv = KT * pt + lane;
+    if (kk >= R) kk = 0;
+    if (kv >= R) kv = 0;
+    const uint64_t krow = reinterpret_cast<uint64_t>(packed_row(kk, true));
+    const uint64_t vrow = reinterpret_cast<uint64_t>(packed_row(kv, false));
+    const uint32_t k_lo = (uint32_t)krow, k_hi = (uint32_t)(krow >> 32);
+    const uint32_t v_lo = (uint32_t)vrow, v_hi = (uint32_t)(vrow >> 32);
 #pragma unroll
     for (int i = 0; i < NDMA; ++i) {
       const int u = (4 * i + wave) * 64 + lane;
       const int r = u / NU, c = u - r * NU;
       const int cb = c < NS ? c * 16 : 0;
-      int kk = KT * pt + key_perm(r < KT ? r : 0), kv = KT * pt + (r < KT ? r : 0);
-      if (kk >= R) kk = 0;
-      if (kv >= R) kv = 0;
-      dma16_flat(packed_row(kk, true) + cb, dma_lds(kdst, i));
-      dma16_flat(packed_row(kv, false) + cb, dma_lds(vdst, i));
+      const int src = r < KT ? r : 0;
+      const uint64_t ka = ((uint64_t)(uint32_t)__shfl((int)k_hi, src, 64) << 32) | (uint32_t)__shfl((int)k_lo, src, 64);
+      const uint64_t va = ((uint64_t)(uint32_t)__shfl((int)v_hi, src, 64) << 32) | (uint32_t)__shfl((int)v_lo, src, 64);
+      dma16_flat_b(reinterpret_cast<const char*>(ka) + cb, dma_lds(kdst, i));
+      dma16_flat_b(reinterpret_cast<const char*>(va) + cb, dma_lds(vdst, i));
     }
   }
 
-  // Q' = bf16(rot(q) * log2(e)/sqrt(d)) as the QK^T B operand.
-  __device__ void init_queries(int qt) {
-    const float sc = p.scale_log2;
+  // Q' = bf16(rot(q) * log2(e)/sqrt(d)) as the QK^T B operand, in two
+  // halves so that other loads can be issued between them: load_queries
+  // issues the raw query chunks and the cos/sin of every pair the lane
+  // holds, rotate_queries rotates, scales and packs them.
+  struct QLoad {
+    uint4 w[2][NC];
+    float2 cs[2][NC][4];
+  };
+  __device__ __forceinline__ void load_queries(int qt, QLoad& L) const {
     const RopeGeom g = p.g;  // in registers: the lookups below must not reload it
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
@@ -375,18 +389,33 @@ struct Attn {
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
         const int off = 16 * c + 8 * hh;
-        const uint4 w = valid ? *reinterpret_cast<const uint4*>(qp + off) : make_uint4(0, 0, 0, 0);
-        uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+        L.w[qb][c] = valid ? *reinterpret_cast<const uint4*>(qp + off) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) L.cs[qb][c][e] = rope_cs(g, off / 2 + e, tq, yq, xq);
+      }
+    }
+  }
+  __device__ __forceinline__ void rotate_queries(const QLoad& L) {
+    const float sc = p.scale_log2;
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        uint32_t ws[4] = {L.w[qb][c].x, L.w[qb][c].y, L.w[qb][c].z, L.w[qb][c].w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float2 cs = rope_cs(g, off / 2 + e, tq, yq, xq);
+          const float2 cs = L.cs[qb][c][e];
           const float x0 = __uint_as_float(ws[e] << 16), x1 = __uint_as_float(ws[e] & 0xffff0000u);
           ws[e] = pack_bf16((x0 * cs.x - x1 * cs.y) * sc, (x0 * cs.y + x1 * cs.x) * sc);
         }
         qreg[qb][c] = __builtin_bit_cast(bf16x8, make_uint4(ws[0], ws[1], ws[2], ws[3]));
       }
-    }
     reset_accumulators();
+  }
+  __device__ void init_queries(int qt) {
+    QLoad L;
+    load_queries(qt, L);
+    rotate_queries(L);
   }
 
   __device__ void reset_accumulators() {
@@ -809,11 +838,15 @@ void attn_bf16_kernel(const AttnParams p) {
 
   bool bad = false;
   if (n_full > 0) {
-    // K and V of tile t go to stage t % 3.  The prologue issues K0, K1, V0,
-    // K2, V1 and the gather of the first packed ragged tile, then rotates the
-    // queries while they land; iteration j issues {K(j+3), V(j+2)} after its
-    // barrier, which waits for every earlier group.  Tiles past the piece's
-    // last one re-read real keys into stages nobody reads.
+    // K and V of tile t go to stage t % 3.  The prologue issues the queries'
+    // loads and their cos/sin lookups first, then K0, K1, V0, K2, V1 and the
+    // gather of the first packed ragged tile, then rotates the queries while
+    // the DMAs land; iteration j issues {K(j+3), V(j+2)} after its barrier,
+    // which waits for every earlier group.  Tiles past the piece's last one
+    // re-read real keys into stages nobody reads.
+    typename A::QLoad ql;
+    a.load_queries(qt, ql);
+    __builtin_amdgcn_sched_barrier(0);
     const size_t head_off = (size_t)head * D * 2;
     const uint32_t tok_bytes = a.tok_bytes, tile_bytes = A::KT * tok_bytes;
     SegCursor ck, cv;  // next K tile to load, next V tile to load
@@ -823,8 +856,8 @@ void attn_bf16_kernel(const AttnParams p) {
     auto load = [&](SegCursor& c, uint32_t stage, const uint32_t (&voff)[A::NDMA], bool is_k) {
 #pragma unroll
       for (int i = 0; i < A::NDMA; ++i)
-        dma16(c.r, i < A::NDMA - 1 || a.last_ok ? stage + (4 * i + a.wave) * 1024 : a.sink(), voff[i],
-              c.off);
+        dma16_b(c.r, i < A::NDMA - 1 || a.last_ok ? stage + (4 * i + a.wave) * 1024 : a.sink(), voff[i],
+                c.off);
       c.next(p, head_off, tok_bytes, tile_bytes, is_k);
     };
     load(ck, kbase, a.voff_k, true);                 // K0
@@ -833,9 +866,8 @@ void attn_bf16_kernel(const AttnParams p) {
     load(ck, kbase + 2 * A::TILE, a.voff_k, true);   // K2
     load(cv, vbase + A::TILE, a.voff_v, false);      // V1
     if (pk1 > pk0) a.dma_packed(pk0, n_ragged, a.pkbuf(), a.pvbuf());
-    // the queries' loads and rotation overlap the DMAs; reading the loaded
-    // queries waits for every earlier load, so all groups have landed here
-    a.init_queries(qt);
+    __builtin_amdgcn_sched_barrier(0);
+    a.rotate_queries(ql);
     wait_vm<0>();
     __syncthreads();
 
