@@ -11,6 +11,9 @@ seeded and resident in HBM before the timed region; the attention inputs of a
 step cycle through pools of 7 distinct Q/K/V sets so consecutive calls do not
 reuse cached keys.
 
+--workload 384x672 runs the same step on the 384x672 bucket (Q=3024,
+K=16128) instead.
+
 Prints one JSON line.  `value` is attention TFLOP/s over the whole step (120
 attention calls' algorithmic FLOPs / block time).  The roofline uses the
 attention kernel alone (attn_kernel_ms): HIP events the library records right
@@ -32,21 +35,25 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "PR-Sink attn ms/call + TFLOP/s (% bf16 MFMA peak), 480×480 block; ms/block stream"
+# --workload 384x672 times the 384x672 bucket (H=40, d=128, 24x42 tokens per
+# frame: Q=3024, K=16128) the same way; 480x480 is the headline workload
+WORKLOADS = ("480x480", "384x672")
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0
 POOL = 7                    # distinct input sets per pool (coprime to the layer count)
 
 
-TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "attn_bf16_kernel_480x480_traffic.json")
 ATTN_SOURCE = os.path.join(ROOT, "bounded_kv_cache_pr_amd", "csrc", "kernels_attn.hip")
 
 
-def measured_traffic():
+def measured_traffic(workload):
     """HBM bytes per attention launch from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE
-    record, or None when the kernel source has changed since it was taken."""
+    record of the workload, or None when there is none or the kernel source has changed
+    since it was taken."""
     import hashlib
+    record = os.path.join(ROOT, "profiles", f"attn_bf16_kernel_{workload}_traffic.json")
     try:
-        with open(TRAFFIC_RECORD) as f:
+        with open(record) as f:
             rec = json.load(f)
         with open(ATTN_SOURCE, "rb") as f:
             sha = hashlib.sha256(f.read()).hexdigest()
@@ -79,8 +86,9 @@ def cpu_baseline(cfg, q, kc, vc, ref_kv_host, block_kv_host, orc, budget_s=12.0)
     flops = attn_flops(cfg) * done / cfg.n_heads
     return {"value": round(flops / t_total / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
             "kind": "oracle",
-            "sample": f"{done} of {cfg.n_heads} heads of one 480x480 attention call "
-                      f"(Q=2700, K=14400, d=128), numpy fp64, {t_total:.1f} s"}
+            "sample": f"{done} of {cfg.n_heads} heads of one {cfg.lat_h * 16}x{cfg.lat_w * 16} "
+                      f"attention call (Q={cfg.block_tokens}, K={cfg.full_cache_keys}, "
+                      f"d={cfg.head_dim}), numpy fp64, {t_total:.1f} s"}
 
 
 def main():
@@ -94,6 +102,7 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--streams", type=int, choices=(1, 2), default=2,
                     help="2: clean-KV writes and the bank update on a second stream")
+    ap.add_argument("--workload", choices=WORKLOADS, default="480x480")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: the PR-Sink path here runs on a single MI355X "
@@ -108,7 +117,8 @@ def main():
     if not os.path.exists(build.LIB_PATH):
         build.build_library()
     dev = torch.device("cuda:0")
-    cfg = synth.C3_STREAM_480.replace(n_layers=args.layers)
+    base = synth.C3_STREAM_480 if args.workload == "480x480" else synth.C2_384x672
+    cfg = base.replace(n_layers=args.layers)
     L, steps = cfg.n_layers, synth.DENOISE_STEPS
     n_blocks = args.warmup + args.steps
     seed = args.seed
@@ -177,8 +187,9 @@ def main():
     achieved = flops / (kern_avg_ms * 1e-3) / 1e12
     value = steps * L * flops / (ms_per_block * 1e-3) / 1e12
 
+    T, Kc = cfg.block_tokens, cfg.full_cache_keys
     result = {
-        "metric": METRIC,
+        "metric": METRIC if args.workload == "480x480" else METRIC.replace("480×480", "384×672"),
         "value": round(value, 3),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -191,8 +202,9 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {
-            "workload": "PR-Sink streamed block at 480x480: H=40, d=128, Q=2700, K=14400 "
-                        f"(Ref 900 + Static/Dynamic/2 window/current 2700 each), {L} layers x "
+            "workload": f"PR-Sink streamed block at {args.workload}: H={cfg.n_heads}, "
+                        f"d={cfg.head_dim}, Q={T}, K={Kc} "
+                        f"(Ref {cfg.ref_tokens} + Static/Dynamic/2 window/current {T} each), {L} layers x "
                         f"{steps} denoise-step attention calls + {L} clean-KV writes + "
                         "retrieval + bank update",
             "blocks_timed": f"{args.warmup}..{n_blocks - 1}",
@@ -212,7 +224,7 @@ def main():
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-            "traffic": measured_traffic(),
+            "traffic": measured_traffic(args.workload),
         },
     }
 
