@@ -625,11 +625,14 @@ int pr_sink_clean_kv_write(pr_sink_cache* c, int32_t layer, const void* k_raw, c
       d.n_rot = 1;
     }
     // the window slot last held block b-W: its last reader was the previous
-    // block's attention, and its bank copy (block b-W's update) came before
-    // that; this block's retrieval waited for both, and this block's own
-    // attention reads other slots, so the write may overlap it
+    // block's attention, which this block's retrieval waited for, and this
+    // block's own attention reads other slots, so the write may overlap it.
+    // Block b-W's bank copy also read the slot: with W >= 2 the retrieval's
+    // wait for block b-2's update covers it, with W = 1 it is the last update,
+    // so the write also waits for the last update's copies.
     hipStream_t s = as_stream(stream);
     PRS_HIP(after(s, c->retr));
+    PRS_HIP(after(s, c->bank));
     PRS_HIP(launch_clean_write(cw, s));
     PRS_HIP(mark(s, c->clean[layer]));
   }

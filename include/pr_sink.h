@@ -48,8 +48,9 @@
  * streams chosen.  The intended split (review, discussion of the Clean KV
  * Update's 24 % share: overlap it) puts pr_sink_clean_kv_write and
  * pr_sink_bank_update on a second stream.  A clean write of block b waits
- * only for block b's retrieval (it fills the slot of block b-W, which block
- * b's attention does not read), so it may overlap block b's attention; block
+ * only for block b's retrieval and the last bank update's copies (it fills
+ * the slot of block b-W, which block b's attention does not read), so it may
+ * overlap block b's attention; block
  * b+1's attention of layer l waits for block b's clean write of layer l; the
  * retrieval of block b+1 waits for block b's bank decision but not for the
  * copy of the entry it writes (that entry holds block b, which the retrieval

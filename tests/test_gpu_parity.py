@@ -199,6 +199,31 @@ def test_bf16_multitile_every_block(cfg):
         st.check_slot_bytes(st.cache.slot_index_bank(i), bid, 1)
 
 
+@pytest.mark.parametrize("window,bank,dtype", [
+    (1, 2, synth.DTYPE_BF16),   # no previous window block; smallest bank
+    (2, 3, synth.DTYPE_BF16),   # one previous block, attended at the newest place only
+    (4, 5, synth.DTYPE_BF16),   # three places: two rotated copies beside the slot's own
+    (5, 8, synth.DTYPE_BF16),   # the most segments (8) and the largest bank
+    (4, 4, synth.DTYPE_F32),
+], ids=["w1m2", "w2m3", "w4m5", "w5m8", "w4m4_f32"])
+def test_window_and_bank_sizes(window, bank, dtype):
+    """Other window and bank sizes than the pages' 3 and 5: every block's attention, the
+    rotated keys at each window place the blocks hold, and the stored bank bytes against the
+    oracle, through the fill phase (8 blocks) into the frozen bank."""
+    cfg = BF16_SMALL.replace(window_slots=window, bank_size=bank, bank_fill_blocks=8, dtype=dtype,
+                             n_heads=3, lat_h=6, lat_w=9)
+    log(f"case: window {window}, bank {bank}, dtype {dtype}, 13 blocks")
+    st = Stream(cfg, seed=13)
+    fps = synth.pose_stream(13, n_protos=7, seed=13)
+    for b in range(13):
+        st.open(b, fps[b])
+        st.check_rotations(b % cfg.n_layers)
+        st.attend_check((b + 1) % cfg.n_layers, step=b % 3)
+        st.close(b)
+    for i, bid in enumerate(st.orc.bank_ids):
+        st.check_slot_bytes(st.cache.slot_index_bank(i), bid, 1)
+
+
 def test_bank_fill_and_freeze_with_swaps():
     """Long enough for swaps (M=5, 20 fill blocks) and the frozen phase; bf16 path."""
     cfg = BF16_SMALL.replace(n_layers=1, n_heads=2, lat_h=4, lat_w=6)
