@@ -185,7 +185,9 @@ BF16_SMALL = synth.PRSinkConfig(n_layers=2, n_heads=4, head_dim=128, rope_dims=(
     BF16_SMALL,                                                   # Q=300: 3 query tiles, ragged
     BF16_SMALL.replace(n_heads=3, head_dim=64, rope_dims=(24, 20, 20), lat_h=5, lat_w=7),  # T=105
     BF16_SMALL.replace(n_heads=9, lat_h=6, lat_w=11, ref_frames=2, block_frames=2, t0=11),
-], ids=["h4d128_q300", "h3d64_q105", "h9d128_ref2_t0"])
+    BF16_SMALL.replace(n_heads=2, lat_h=8, lat_w=8),   # every segment a multiple of 64 keys: no ragged tile
+    BF16_SMALL.replace(n_heads=2, lat_h=3, lat_w=5),   # every segment under 64 keys: only ragged tiles
+], ids=["h4d128_q300", "h3d64_q105", "h9d128_ref2_t0", "h2_noragged", "h2_allragged"])
 def test_bf16_multitile_every_block(cfg):
     log(f"case: bf16 multi-tile {cfg}")
     st = Stream(cfg, seed=5)
