@@ -211,16 +211,18 @@ def test_mean_pairwise_similarity_closed_forms():
         assert abs(O.mean_pairwise_similarity(phis) - closed) < 1e-14
 
 
-def test_bank_decision_is_exhaustive_argmin():
-    rng = np.random.default_rng(8)
+@pytest.mark.parametrize("M", [2, 3, 5, 8])
+def test_bank_decision_is_exhaustive_argmin(M):
+    rng = np.random.default_rng(8 + M)
     for _ in range(100):
         bank = [O.fingerprint(np.abs(rng.standard_normal(558)) + rng.uniform(0, 2) * _onehot(int(rng.integers(558))))
-                for _ in range(5)]
+                for _ in range(M)]
         phi = O.fingerprint(np.abs(rng.standard_normal(558)))
-        kind, slot = O.bank_decision(bank, phi, 5)
-        gram_s = lambda B: (np.sum(np.array(B) @ np.array(B).T) - 5.0) / 20.0  # unit vectors: trace = 5
+        kind, slot = O.bank_decision(bank, phi, M)
+        # mean over the M(M-1)/2 unordered pairs from the Gram matrix of unit vectors (trace = M)
+        gram_s = lambda B: (np.sum(np.array(B) @ np.array(B).T) - M) / (M * (M - 1))
         opts = [("keep", None, gram_s(bank))] + [
-            ("swap", j, gram_s(bank[:j] + [phi] + bank[j + 1:])) for j in range(5)]
+            ("swap", j, gram_s(bank[:j] + [phi] + bank[j + 1:])) for j in range(M)]
         best = min(opts, key=lambda o: o[2])
         assert abs(best[2] - dict(((o[0], o[1]), o[2]) for o in opts)[(kind, slot)]) < 1e-13
         if kind == "swap":
@@ -280,6 +282,32 @@ def test_cache_keys_per_config():
     assert synth.C0_TINY.full_cache_keys == 176 and synth.C0_TINY.block_tokens == 32
     assert synth.C1_480.full_cache_keys == 14400 and synth.C1_480.block_tokens == 2700
     assert synth.C2_384x672.full_cache_keys == 16128 and synth.C2_384x672.block_tokens == 3024
+
+
+@pytest.mark.parametrize("window", [1, 2, 3, 4, 5])
+def test_segment_layout_closed_form_per_window_size(window):
+    """The layout for any window size, written out: Ref at t0, then Static, Dynamic, the
+    W-1 previous blocks oldest first and the current block, each block_frames long and
+    back to back; a previous block that does not exist yet is absent but keeps its place.
+    Checked at every block of a short stream against this closed form (not the oracle's own
+    loop): the window holds exactly blocks b-W+1 .. b-1."""
+    cfg = synth.C0_TINY.replace(window_slots=window, ref_frames=2, block_frames=3, t0=5)
+    orc = O.PRSinkOracle(cfg)
+    fps = synth.pose_stream(9, seed=3)
+    for b in range(9):
+        orc.open_block(b, fps[b])
+        segs = orc.segment_layout()
+        assert len(segs) == window + 3
+        kinds = [sg[0] for sg in segs]
+        assert kinds == [O.SEG_REF, O.SEG_STATIC, O.SEG_DYNAMIC] + [O.SEG_WINDOW] * (window - 1) + [O.SEG_CURRENT]
+        starts = [sg[2] for sg in segs]
+        assert starts == [5] + [5 + 2 + 3 * i for i in range(window + 2)]
+        assert [sg[3] for sg in segs] == [2] + [3] * (window + 2)
+        win = [(sg[1], sg[4]) for sg in segs if sg[0] == O.SEG_WINDOW]
+        assert win == [(b - window + 1 + j, b - window + 1 + j >= 0) for j in range(window - 1)]
+        assert segs[1][4] == (b >= 1) and segs[1][1] == (0 if b >= 1 else None)
+        assert segs[-1][1] == b
+        orc.close_block(b)
 
 
 def test_stream_bank_and_window_invariants():
