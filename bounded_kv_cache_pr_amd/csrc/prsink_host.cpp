@@ -15,6 +15,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <exception>
 #include <new>
 #include <string>
 #include <vector>
@@ -377,8 +378,27 @@ size_t pr_sink_arena_bytes(const pr_sink_config* cfg) {
   return make_layout(cfg).total;
 }
 
+namespace {
+int cache_init(const pr_sink_config* cfg, void* arena_dev, size_t arena_bytes, void* stream,
+               pr_sink_cache** out);
+}  // namespace
+
+// The only call that allocates host memory (the cos/sin table, per-layer
+// state): an allocation failure returns an error instead of leaving the C ABI
+// as an exception.
 int pr_sink_cache_init(const pr_sink_config* cfg, void* arena_dev, size_t arena_bytes,
                        void* stream, pr_sink_cache** out) {
+  try {
+    return cache_init(cfg, arena_dev, arena_bytes, stream, out);
+  } catch (const std::exception& e) {
+    if (out) *out = nullptr;
+    return fail(PR_SINK_EINVAL, "host allocation failed: %s", e.what());
+  }
+}
+
+namespace {
+int cache_init(const pr_sink_config* cfg, void* arena_dev, size_t arena_bytes, void* stream,
+               pr_sink_cache** out) {
   if (!out) return fail(PR_SINK_EINVAL, "out is NULL");
   *out = nullptr;
   if (!check_config(cfg)) return PR_SINK_EINVAL;
@@ -417,7 +437,12 @@ int pr_sink_cache_init(const pr_sink_config* cfg, void* arena_dev, size_t arena_
   c->bank_count = 0;
   c->dyn_present = false;
   c->n_cu = n_cu;
-  c->clean.resize(cfg->n_layers);
+  try {
+    c->clean.resize(cfg->n_layers);
+  } catch (...) {
+    delete c;
+    throw;
+  }
   if (!dry) {
     auto make = [](pr_sink_cache::Mark& m) { return hipEventCreateWithFlags(&m.ev, hipEventDisableTiming); };
     hipError_t e = hipSuccess;
@@ -429,12 +454,18 @@ int pr_sink_cache_init(const pr_sink_config* cfg, void* arena_dev, size_t arena_
       return fail(PR_SINK_EHIP, "hipEventCreateWithFlags: %s", hipGetErrorString(e));
     }
   }
-  c->ref_set.assign(cfg->n_layers, 0);
-  c->written.assign(cfg->n_layers, 0);
+  try {
+    c->ref_set.assign(cfg->n_layers, 0);
+    c->written.assign(cfg->n_layers, 0);
+  } catch (...) {
+    delete c;
+    throw;
+  }
   *out = c;
   g_err.clear();
   return PR_SINK_OK;
 }
+}  // namespace
 
 int pr_sink_set_ref(pr_sink_cache* c, int32_t layer, const void* k_raw, const void* v_raw,
                     void* stream) {
