@@ -172,8 +172,8 @@ class PRSinkCache:
             torch = _torch()
             if fp_raw.dtype != torch.float32 or fp_raw.numel() != self.cfg.fp_dim:
                 raise ValueError("fp_raw must be float32[fp_dim]")
-            if slot_out is not None and slot_out.dtype != torch.int32:
-                raise ValueError("slot_out must be int32")
+            if slot_out is not None and (slot_out.dtype != torch.int32 or slot_out.numel() < 1):
+                raise ValueError("slot_out must be int32 with at least one element")
         so = None if slot_out is None else self._ptr(slot_out, None, "slot_out")
         check(lib().pr_sink_retrieve(self._h, block, self._ptr(fp_raw, None, "fp_raw"), so,
                                      self._stream()))
