@@ -38,6 +38,7 @@
  * Tensor layout at the boundary: q, k, v, out are contiguous [T][H][d] in the
  * config's element type (bf16 or f32), T = block_frames*lat_h*lat_w tokens in
  * (frame, row, column) order; Ref tensors have T = ref_frames*lat_h*lat_w.
+ * Every tensor pointer must be 16-byte aligned (PR_SINK_EINVAL otherwise).
  *
  * Streams: every call is asynchronous on `stream` (a hipStream_t passed as
  * void*; NULL = the null stream) except pr_sink_cache_init and
