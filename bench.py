@@ -46,10 +46,11 @@ POOL = 7                    # distinct input sets per pool (coprime to the layer
 ATTN_SOURCE = os.path.join(ROOT, "bounded_kv_cache_pr_amd", "csrc", "kernels_attn.hip")
 
 
-def measured_traffic(workload):
-    """HBM bytes per attention launch from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE
-    record of the workload, or None when there is none or the kernel source has changed
-    since it was taken."""
+def counter_record(workload):
+    """The committed rocprofv3 counter record of the workload (HBM bytes per attention
+    launch from FETCH_SIZE / WRITE_SIZE; the shader clock and MFMA utilisation where
+    measured), or None when there is none or the kernel source has changed since it was
+    taken."""
     import hashlib
     record = os.path.join(ROOT, "profiles", f"attn_bf16_kernel_{workload}_traffic.json")
     try:
@@ -59,7 +60,7 @@ def measured_traffic(workload):
             sha = hashlib.sha256(f.read()).hexdigest()
     except OSError:
         return None
-    return rec["traffic_bytes_per_launch"] if rec.get("kernels_attn_hip_sha256") == sha else None
+    return rec if rec.get("kernels_attn_hip_sha256") == sha else None
 
 
 def attn_flops(cfg) -> float:
@@ -224,9 +225,22 @@ def main():
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-            "traffic": measured_traffic(args.workload),
+            "traffic": None,
         },
     }
+    rec = counter_record(args.workload)
+    if rec is not None:
+        result["roofline"]["traffic"] = rec["traffic_bytes_per_launch"]
+        if "shader_clock_ghz" in rec:
+            # the same MFMA peak at the shader clock the counters saw during this kernel
+            peak_clk = PEAK_BF16_TFLOPS * rec["shader_clock_ghz"] / 2.4
+            result["clock_adjusted"] = {
+                "shader_clock_ghz": rec["shader_clock_ghz"],
+                "peak_tflops_at_clock": round(peak_clk, 1),
+                "frac": round(achieved / peak_clk, 4),
+                "mfma_util_pct": rec.get("mfma_util_pct"),
+                "source": f"profiles/attn_bf16_kernel_{args.workload}_traffic.json",
+            }
 
     if not args.no_cpu_baseline:
         import oracle as O
