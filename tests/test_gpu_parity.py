@@ -349,6 +349,40 @@ def test_common_temporal_shift():
     assert rel_l2(outs[1], outs[0]) <= BF16_REL
 
 
+def test_attend_events_bracket_the_kernel():
+    """pr_sink_set_attend_events: the caller's events are recorded right around the attention
+    kernel on the call's stream, so their interval is positive and shorter than the whole call
+    (which also rotates the current keys); clearing them stops the recording."""
+    cfg = BF16_SMALL.replace(n_layers=1, n_heads=8, lat_h=16, lat_w=16)
+    log("case: attend events")
+    st = Stream(cfg, seed=3)
+    fps = synth.pose_stream(3, seed=3)
+    for b in range(2):
+        st.open(b, fps[b])
+        st.close(b)
+    st.open(2, fps[2])
+    q, kc, vc = (to_dev(x, st.dt) for x in synth.step_qkv(cfg, 2, 0, 0, 3))
+    k0, k1, c0, c1 = (torch.cuda.Event(enable_timing=True) for _ in range(4))
+    stream = torch.cuda.current_stream(DEV)
+    for e in (k0, k1):
+        e.record(stream)  # created before handing over
+    torch.cuda.synchronize()
+    st.cache.set_attend_events(k0, k1)
+    c0.record(stream)
+    st.cache.attend(0, q, kc, vc)
+    c1.record(stream)
+    torch.cuda.synchronize()
+    kernel_ms, call_ms = k0.elapsed_time(k1), c0.elapsed_time(c1)
+    assert 0.0 < kernel_ms < call_ms, (kernel_ms, call_ms)
+    st.cache.set_attend_events()
+    k1.record(stream)  # a later recording of the caller's own...
+    torch.cuda.synchronize()
+    marker = k0.elapsed_time(k1)
+    st.cache.attend(0, q, kc, vc)
+    torch.cuda.synchronize()
+    assert k0.elapsed_time(k1) == marker  # ...is not moved by the library any more
+
+
 def test_device_errors_leave_state_unchanged():
     cfg = BF16_SMALL.replace(n_layers=1)
     log("case: error paths on a device cache")
