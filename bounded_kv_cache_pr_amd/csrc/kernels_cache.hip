@@ -13,6 +13,20 @@
 namespace prsink {
 namespace {
 
+// Streaming 16-byte accesses (the nt bit): what the clean write and the bank
+// copy read is read once, and what they write is read back only blocks later,
+// so neither should evict from L2 the keys that attention running beside them
+// streams.
+typedef unsigned int u32x4_nt __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 ld_nt(const uint4* p) {
+  const u32x4_nt v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_nt*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void st_nt(uint4* p, uint4 w) {
+  const u32x4_nt v = {w.x, w.y, w.z, w.w};
+  __builtin_nontemporal_store(v, reinterpret_cast<u32x4_nt*>(p));
+}
+
 // ---------------------------------------------------------------------------
 // kv_write: raw K and V [T][H][d] -> slot layout [t_pad][H][d] (the same
 // token-major order, so a contiguous copy), optionally to a second
@@ -48,10 +62,14 @@ __global__ __launch_bounds__(256) void slot_copy_kernel(uint8_t* __restrict__ ba
   const size_t stride = (size_t)gridDim.x * blockDim.x;
   size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   for (; i + 3 * stride < n; i += 4 * stride) {
-    const uint4 a = s[i], b = s[i + stride], c = s[i + 2 * stride], e = s[i + 3 * stride];
-    d[i] = a; d[i + stride] = b; d[i + 2 * stride] = c; d[i + 3 * stride] = e;
+    const uint4 a = ld_nt(s + i), b = ld_nt(s + i + stride), c = ld_nt(s + i + 2 * stride),
+                e = ld_nt(s + i + 3 * stride);
+    st_nt(d + i, a);
+    st_nt(d + i + stride, b);
+    st_nt(d + i + 2 * stride, c);
+    st_nt(d + i + 3 * stride, e);
   }
-  for (; i < n; i += stride) d[i] = s[i];
+  for (; i < n; i += stride) st_nt(d + i, ld_nt(s + i));
 }
 
 // ---------------------------------------------------------------------------
@@ -142,19 +160,19 @@ __global__ __launch_bounds__(256) void clean_write_kernel(const CleanWrite p) {
   for (uint32_t i = blockIdx.x * 256 + threadIdx.x; i < total; i += stride) {
     const uint32_t n = i / per_tok;
     const uint32_t c = (i - n * per_tok) % per_head;
-    const uint4 k = ks[i], v = vs[i];
+    const uint4 k = ld_nt(ks + i), v = ld_nt(vs + i);
 #pragma unroll
     for (int d = 0; d < 2; ++d) {
       const CleanDst& o = p.dst[d];
       if (!o.k) continue;
-      reinterpret_cast<uint4*>(o.k)[i] = k;
-      reinterpret_cast<uint4*>(o.v)[i] = v;
+      st_nt(reinterpret_cast<uint4*>(o.k) + i, k);
+      st_nt(reinterpret_cast<uint4*>(o.v) + i, v);
 #pragma unroll
       for (int r = 0; r < kMaxRot; ++r) {
         if (r >= o.n_rot) break;
         int tt, y, x;
         token_pos(p.g, (int)n, o.t_index[r], tt, y, x);
-        reinterpret_cast<uint4*>(o.k_rot[r])[i] = rotate_chunk(p.g, k, c, p.elem, tt, y, x);
+        st_nt(reinterpret_cast<uint4*>(o.k_rot[r]) + i, rotate_chunk(p.g, k, c, p.elem, tt, y, x));
       }
     }
   }
