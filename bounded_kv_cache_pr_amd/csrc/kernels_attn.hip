@@ -680,23 +680,42 @@ struct Attn {
   }
 
   __device__ void epilogue(int qt) {
+    // The normalised bf16 rows go through this wave's own LDS region, so each
+    // global store writes whole 256-byte rows (16 lanes a row) instead of 16
+    // bytes in each of 32 rows.  Every wave has passed a barrier after its
+    // last read of the ring and no DMA is in flight, so the region is free.
     // register 4g+e of dv block db is dv = 32db + 8g + 4hh + e
+    constexpr int OS = RB + 16;  // LDS row stride (16-byte aligned rows)
+    char* const ob = smem + wave * 64 * OS;
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
-      const int qrow = qt * QT + wave * 64 + qb * 32 + l32;
       const float l_tot = l_run[qb] + __shfl_xor(l_run[qb], 32, 64);
       const float inv = 1.0f / l_tot;
-      if (qrow < p.n_q) {
-        uint16_t* op = static_cast<uint16_t*>(p.out) + ((size_t)qrow * p.n_heads + head) * D;
+      char* const orow = ob + (qb * 32 + l32) * OS + hh * 8;
 #pragma unroll
-        for (int db = 0; db < NDB; ++db)
+      for (int db = 0; db < NDB; ++db)
 #pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const uint2 w = make_uint2(pack_bf16(o[qb][db][4 * g] * inv, o[qb][db][4 * g + 1] * inv),
-                                       pack_bf16(o[qb][db][4 * g + 2] * inv, o[qb][db][4 * g + 3] * inv));
-            *reinterpret_cast<uint2*>(op + db * 32 + g * 8 + hh * 4) = w;
-          }
-      }
+        for (int g = 0; g < 4; ++g)
+          *reinterpret_cast<uint2*>(orow + db * 64 + g * 16) =
+              make_uint2(pack_bf16(o[qb][db][4 * g] * inv, o[qb][db][4 * g + 1] * inv),
+                         pack_bf16(o[qb][db][4 * g + 2] * inv, o[qb][db][4 * g + 3] * inv));
+    }
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    constexpr int RPI = 64 / NS;  // rows per store instruction
+    const int c = lane % NS;
+    const int row0 = qt * QT + wave * 64 + lane / NS;
+    char* const out0 = static_cast<char*>(p.out) + ((size_t)row0 * p.n_heads + head) * RB + c * 16;
+    const size_t step = (size_t)RPI * p.n_heads * RB;
+    const char* const in0 = ob + (lane / NS) * OS + c * 16;
+    if (qt * QT + wave * 64 + 64 <= p.n_q) {  // every row of the wave is a query
+#pragma unroll
+      for (int i = 0; i < 64 / RPI; ++i)
+        *reinterpret_cast<uint4*>(out0 + i * step) = *reinterpret_cast<const uint4*>(in0 + i * RPI * OS);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 64 / RPI; ++i)
+        if (row0 + i * RPI < p.n_q)
+          *reinterpret_cast<uint4*>(out0 + i * step) = *reinterpret_cast<const uint4*>(in0 + i * RPI * OS);
     }
   }
 };

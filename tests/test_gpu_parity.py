@@ -349,6 +349,57 @@ def test_common_temporal_shift():
     assert rel_l2(outs[1], outs[0]) <= BF16_REL
 
 
+# First element of the last RoPE pair of each band at d = 128 (bands 44/42/42):
+# its frequency is theta^(-(D_a - 2)/D_a), about 1.5e-4, so at these
+# positions the pair turns by under 0.005 rad and the product of two such
+# pairs keeps its sign and size.
+_SLOW_PAIRS = (42, 84, 126)
+
+
+@pytest.mark.parametrize("amp", [8.0, 16.0], ids=["weights_2e27", "sum_past_2e64"])
+def test_first_tile_far_below_the_rest(amp, monkeypatch):
+    """The Ref Sink's keys score far below every other key (queries carry +amp and the
+    Ref keys -amp in the three slow pairs; the other keys carry 0 there), so the first
+    tile's row max, which the attention kernel keeps as its reference, sits 24 (amp 8)
+    or 98 (amp 16) below the real one, in log2 units.  At amp 8 the weights reach
+    2^27 against that reference and stay in range; at amp 16 the row sums pass the
+    2^64 limit and the kernel redoes the row blocks with exact online softmax.  Both
+    must match the oracle."""
+    cfg = BF16_SMALL.replace(n_layers=1)
+    ref_kv, clean_kv, step_qkv = synth.ref_kv, synth.clean_kv, synth.step_qkv
+    slow, slow1 = list(_SLOW_PAIRS), [i + 1 for i in _SLOW_PAIRS]
+
+    def ref_low(c, layer, seed):
+        k, v = ref_kv(c, layer, seed)
+        k = k.copy()
+        k[..., slow], k[..., slow1] = -amp, 0.0
+        return k, v
+
+    def clean_flat(c, block, layer, seed):
+        k, v = clean_kv(c, block, layer, seed)
+        k = k.copy()
+        k[..., slow + slow1] = 0.0
+        return k, v
+
+    def step_high(c, block, step, layer, seed):
+        q, k, v = step_qkv(c, block, step, layer, seed)
+        q, k = q.copy(), k.copy()
+        q[..., slow], q[..., slow1] = amp, 0.0
+        k[..., slow + slow1] = 0.0
+        return q, k, v
+
+    monkeypatch.setattr(synth, "ref_kv", ref_low)
+    monkeypatch.setattr(synth, "clean_kv", clean_flat)
+    monkeypatch.setattr(synth, "step_qkv", step_high)
+    log(f"case: first tile far below the rest, amp {amp}")
+    st = Stream(cfg, seed=29)
+    fps = synth.pose_stream(5, seed=29)
+    for b in range(5):
+        st.open(b, fps[b])
+        st.attend_check(0, step=b % 3)
+        st.close(b)
+
+
 def test_attend_events_bracket_the_kernel():
     """pr_sink_set_attend_events: the caller's events are recorded right around the attention
     kernel on the call's stream, so their interval is positive and shorter than the whole call
