@@ -3,6 +3,7 @@ declares, and validates configs, arguments and call order without a GPU
 (dry-run caches never touch a device)."""
 import os
 import re
+import sys
 
 import pytest
 
@@ -171,3 +172,13 @@ def test_no_bank_means_no_dynamic_sink():
         for l in range(cfg.n_layers):
             c.clean_kv_write(l, FAKE, FAKE)
         c.bank_update(b)
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py measures one GPU: --gpus above 1 exits with a message before touching a device."""
+    import subprocess
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    res = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"],
+                         capture_output=True, text=True, timeout=60)
+    assert res.returncode == 2
+    assert "one GPU" in res.stderr and res.stdout == ""
