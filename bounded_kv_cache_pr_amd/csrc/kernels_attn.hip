@@ -582,20 +582,6 @@ struct Attn {
     return __builtin_bit_cast(bf16x8, __builtin_shufflevector(h[0], h[1], 0, 1, 2, 3, 4, 5, 6, 7));
   }
 
-  // Packed softmax pair e (elements 2e, 2e+1) of a 16-score block already
-  // shifted by -m: returns the packed bf16 word, adds its two (rounded)
-  // values to acc.  The sum uses shifts and fp32 adds: a v_dot2 between MFMAs
-  // stalls the matrix pipe for far longer.  The empty asm keeps the work in
-  // the step that issues it (the compiler would otherwise sink it next to its
-  // first use, a whole group later).
-  __device__ __forceinline__ uint32_t soft_pair(const f32x16& s, int e, float& acc) const {
-    uint32_t w = pack_bf16(__builtin_amdgcn_exp2f(s[2 * e]), __builtin_amdgcn_exp2f(s[2 * e + 1]));
-    acc += __uint_as_float(w << 16);
-    acc += __uint_as_float(w & 0xffff0000u);
-    asm volatile("" : "+v"(w), "+v"(acc));
-    return w;
-  }
-
   static __device__ __forceinline__ bf16x8 words(const uint32_t (&w)[4]) {
     return __builtin_bit_cast(bf16x8, make_uint4(w[0], w[1], w[2], w[3]));
   }
@@ -924,15 +910,14 @@ void attn_bf16_kernel(const AttnParams p) {
     // operands can be read before the iteration ends; then the group
     // {K(j+3), V(j+2)} is issued, one DMA per step of groups C and D.
     //
-    // Softmax runs as a five-stage software pipeline over the 32 packed pairs
+    // Softmax runs as a two-stage software pipeline over the 32 packed pairs
     // of an iteration (pairs 0..7: s_hi of query block 0, 8..15: s_hi of block
-    // 1, 16..23 / 24..31: the new keys 0..31 of blocks 0 / 1): stage k of
-    // pair q runs PAIRS-per-step k steps after its read, so no instruction
-    // waits on a result issued in the same step and the MFMAs keep issuing.
-    // Stages: 0 read the scores, 1 exp2, 2 pack to bf16 (the PV operand word),
-    // 3 unpack the rounded halves, 4 add them to the row sums.  The last
-    // stages of an iteration's final pairs run in the next iteration's first
-    // steps (or in the drain).
+    // 1, 16..23 / 24..31: the new keys 0..31 of blocks 0 / 1): stage 0
+    // exponentiates a pair's two scores, stage 1, one step later, packs them
+    // to bf16 (the PV operand word) and adds the fp32 exponentials to the row
+    // sums, so no instruction waits on a result issued in the same step and
+    // the MFMAs keep issuing.  Stage 1 of an iteration's last pairs runs in
+    // the next iteration's first step (or in the drain).
     using SP = SoftPipe<A>;
     SP sp;
     sp.init(pb, l0, l1, s_hi);
