@@ -182,3 +182,25 @@ def test_bench_refuses_more_than_one_gpu():
                          capture_output=True, text=True, timeout=60)
     assert res.returncode == 2
     assert "one GPU" in res.stderr and res.stdout == ""
+
+
+def test_bench_counter_record_follows_the_kernel_source(tmp_path, monkeypatch):
+    """bench.py reports a rocprofv3 counter record (HBM bytes, clock) only while the attention
+    kernel's source hash matches the one the record was taken on."""
+    import hashlib
+    import json
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    sys.path.insert(0, root)
+    import bench
+    src = tmp_path / "kernels_attn.hip"
+    src.write_bytes(b"// kernel source\n")
+    (tmp_path / "profiles").mkdir()
+    rec = {"kernels_attn_hip_sha256": hashlib.sha256(src.read_bytes()).hexdigest(),
+           "traffic_bytes_per_launch": 409636192, "shader_clock_ghz": 1.956}
+    (tmp_path / "profiles" / "attn_bf16_kernel_480x480_traffic.json").write_text(json.dumps(rec))
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    monkeypatch.setattr(bench, "ATTN_SOURCE", str(src))
+    assert bench.counter_record("480x480") == rec
+    assert bench.counter_record("384x672") is None          # no record for that workload
+    src.write_bytes(b"// kernel source, changed\n")
+    assert bench.counter_record("480x480") is None          # the kernel changed since
