@@ -15,12 +15,12 @@ reuse cached keys.
 K=16128) instead.
 
 Prints one JSON line.  `value` is attention TFLOP/s over the whole step (120
-attention calls' algorithmic FLOPs / block time).  The roofline uses the
-attention kernel alone (attn_kernel_ms): HIP events the library records right
-around each launch of the timed blocks.  The whole pr_sink_attend call
-(attn_ms_per_call: rotation of the current keys + attention kernel) is timed
-with HIP events on one extra block after the timed region, so the timed blocks
-carry no extra markers.
+attention calls' algorithmic FLOPs / block time).  The timed blocks carry no
+timing markers.  After them, untimed blocks of the same stream measure the
+whole pr_sink_attend call (attn_ms_per_call: rotation of the current keys +
+attention kernel; one block, HIP events around each call) and the attention
+kernel alone (attn_kernel_ms, which the roofline uses; two blocks, HIP events
+the library records right around each launch).
 """
 from __future__ import annotations
 
@@ -41,6 +41,7 @@ WORKLOADS = ("480x480", "384x672")
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0
 POOL = 7                    # distinct input sets per pool (coprime to the layer count)
+KERNEL_BLOCKS = 2           # untimed blocks whose attention kernels carry HIP events
 
 
 ATTN_SOURCE = os.path.join(ROOT, "bounded_kv_cache_pr_amd", "csrc", "kernels_attn.hip")
@@ -131,7 +132,7 @@ def main():
     qkv_pool = [synth.step_qkv_torch(cfg, 10_000 + i, 0, 0, seed, dev) for i in range(POOL)]
     clean_pool = [synth.clean_kv_torch(cfg, 20_000 + i, 0, seed, dev) for i in range(POOL)]
     out = torch.empty_like(qkv_pool[0][0])
-    fps = torch.from_numpy(synth.pose_stream(n_blocks + 1, seed=seed)).to(dev)
+    fps = torch.from_numpy(synth.pose_stream(n_blocks + 1 + KERNEL_BLOCKS, seed=seed)).to(dev)
     stream = torch.cuda.current_stream(dev)
     clean_stream = torch.cuda.Stream(dev) if args.streams == 2 else stream
     # whole-call events, recorded on one extra block after the timed region so
@@ -141,7 +142,7 @@ def main():
     # events the library records right around its attention kernel (the
     # kernel alone, without the rotation of the current keys before it)
     kev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(steps * L * args.steps)]
+           for _ in range(steps * L * KERNEL_BLOCKS)]
     for a, z in kev:  # create the events before handing them over
         a.record(stream)
         z.record(stream)
@@ -172,12 +173,14 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        run_block(args.warmup + i, kernel_base=i * steps * L)
+        run_block(args.warmup + i)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    cache.set_attend_events()
     run_block(n_blocks, call_events=True)   # untimed: whole-call durations
+    for i in range(KERNEL_BLOCKS):          # untimed: attention kernel durations
+        run_block(n_blocks + 1 + i, kernel_base=i * steps * L)
     torch.cuda.synchronize()
+    cache.set_attend_events()
 
     ms_per_block = (t1 - t0) * 1e3 / args.steps
     attn_ms = [a.elapsed_time(b) for a, b in ev]
