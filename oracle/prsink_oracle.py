@@ -136,15 +136,33 @@ def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float,
 # ----------------------------------------------------------------------------
 # Fingerprint, retrieval and the diversity bank
 # ----------------------------------------------------------------------------
+def seq_dot(a, b) -> float:
+    """sum_k a[k] * b[k] as written: k = 0, 1, 2, ... in order, every product and
+    every partial sum rounded to fp64 (Python floats: no fused multiply-add, no
+    pairwise or blocked summation).  Used for the squared norm of a fingerprint
+    and for every fingerprint dot product, so that the result has one definition
+    and any other implementation that adds in index order reproduces it bit for
+    bit (review, full-pipeline paragraph: l2-normalised fingerprints compared by
+    dot product)."""
+    s = 0.0
+    for x, y in zip(np.asarray(a, np.float64).ravel().tolist(),
+                    np.asarray(b, np.float64).ravel().tolist()):
+        s += x * y
+    return s
+
+
 def fingerprint(x_raw: np.ndarray) -> np.ndarray:
-    """phi = x / ||x||_2 in fp64; an all-zero fingerprint stays zero."""
+    """phi = x / ||x||_2 in fp64, ||x||_2 = sqrt of the index-order sum of x_k^2
+    (correctly rounded square root, then one correctly rounded division per
+    element); an all-zero fingerprint stays zero."""
     x = np.asarray(x_raw, dtype=np.float64).ravel()
-    n = math.sqrt(float(np.dot(x, x)))
+    n = math.sqrt(seq_dot(x, x))
     return x / n if n > 0.0 else np.zeros_like(x)
 
 
 def retrieval_scores(phi_b: np.ndarray, bank_phi) -> np.ndarray:
-    return np.array([float(np.dot(phi_b, p)) for p in bank_phi], dtype=np.float64)
+    """phi_b . phi_i for every bank entry, each an index-order sum."""
+    return np.array([seq_dot(phi_b, p) for p in bank_phi], dtype=np.float64)
 
 
 def retrieve(phi_b: np.ndarray, bank_ids, bank_phi, block: int):
@@ -169,7 +187,7 @@ def mean_pairwise_similarity(phis) -> float:
     tot, cnt = 0.0, 0
     for i in range(n):
         for j in range(i + 1, n):
-            tot += float(np.dot(phis[i], phis[j]))
+            tot += seq_dot(phis[i], phis[j])
             cnt += 1
     return tot / cnt
 

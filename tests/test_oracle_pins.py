@@ -147,17 +147,51 @@ def test_frame_positions_order():
 # ---------------------------------------------------------------------------
 # Fingerprint, retrieval, bank
 # ---------------------------------------------------------------------------
+def test_seq_dot_is_the_index_order_sum():
+    """seq_dot adds the rounded products in index order, nothing else:
+    * integer-valued inputs whose partial sums stay below 2^53 give the exact
+      integer dot product;
+    * [1e16, 1, -1e16] . [1, 1, 1] is 0 in index order (1e16 + 1 rounds back to
+      1e16, whose ulp is 2), while the exact value and a pairwise or reordered
+      sum give 1: this pins the order;
+    * on random inputs the result lies within the textbook bound of recursive
+      summation, |s - exact| <= gamma_n * sum |a_k b_k| with
+      gamma_n = n u / (1 - n u), u = 2^-53, against exact rational arithmetic;
+    * products commute bit for bit, so a . b == b . a."""
+    from fractions import Fraction
+    rng = np.random.default_rng(31)
+    a = rng.integers(-1000, 1000, 558).astype(np.float64)
+    b = rng.integers(-1000, 1000, 558).astype(np.float64)
+    assert O.seq_dot(a, b) == float(sum(int(x) * int(y) for x, y in zip(a, b)))
+    assert O.seq_dot([1e16, 1.0, -1e16], [1.0, 1.0, 1.0]) == 0.0
+    assert math.fsum([1e16, 1.0, -1e16]) == 1.0
+    u = 2.0 ** -53
+    for n in (3, 62, 558):
+        for _ in range(20):
+            a, b = rng.standard_normal(n), rng.standard_normal(n)
+            exact = sum(Fraction(float(x)) * Fraction(float(y)) for x, y in zip(a, b))
+            gamma = n * u / (1 - n * u)
+            bound = gamma * float(sum(abs(Fraction(float(x)) * Fraction(float(y))) for x, y in zip(a, b)))
+            assert abs(Fraction(O.seq_dot(a, b)) - exact) <= Fraction(bound)
+            assert O.seq_dot(a, b) == O.seq_dot(b, a)
+
+
 def test_fingerprint_closed_forms():
     x = np.zeros(558, np.float32); x[0], x[5] = 3.0, 4.0
     phi = O.fingerprint(x)
     assert phi[0] == 0.6 and phi[5] == 0.8 and np.count_nonzero(phi) == 2
     assert not O.fingerprint(np.zeros(558, np.float32)).any()
     fps = synth.pose_stream(20, seed=9)
+    # ||phi|| = 1 up to the rounding of the index-order squared norm (gamma_n with
+    # n = 558, halved by the square root), of the square root and of the divisions,
+    # and of numpy's own norm: 2 n u covers all of it
+    tol = 2 * 558 * 2.0 ** -53
     for f in fps:
         phi = O.fingerprint(f)
         if f.any():
-            assert abs(np.linalg.norm(phi) - 1.0) < 1e-15
-            np.testing.assert_allclose(O.fingerprint(f * np.float32(4.0)), phi, atol=1e-16)
+            assert abs(np.linalg.norm(phi) - 1.0) <= tol
+            # scaling by a power of two scales every partial sum exactly: same bits
+            assert np.array_equal(O.fingerprint(f * np.float32(4.0)), phi)
 
 
 def _onehot(i, n=558):
