@@ -8,7 +8,7 @@
 //                round trip
 //   retrieve     fingerprint l2-normalisation + argmax over the bank (fp64)
 //   bank_update  exhaustive diversity replacement (fp64)
-#include "prsink_internal.h"
+#include "prsink_device.h"
 
 namespace prsink {
 namespace {
@@ -179,43 +179,45 @@ __global__ __launch_bounds__(256) void clean_write_kernel(const CleanWrite p) {
 }
 
 // ---------------------------------------------------------------------------
-// fp64 wave-64 helpers.  Reductions run a fixed butterfly, so results are
-// reproducible bit for bit from run to run.
+// Fingerprint arithmetic (fp64).  Every squared norm and dot product is the
+// plain sum of the rounded products in index order, k = 0, 1, 2, ..., with no
+// fused multiply-add: one lane per sum.  That is the definition itself, so any
+// implementation that adds in the same order gets the same bits, and the
+// retrieval and bank decisions never depend on how a reduction was split.
 // ---------------------------------------------------------------------------
-__device__ inline double wave_sum(double v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
-  return v;
-}
-
-__device__ inline double dot_f64(const double* __restrict__ a, const double* __restrict__ b,
-                                 int n, int lane) {
-  double acc = 0.0;
-  for (int k = lane; k < n; k += 64) acc += a[k] * b[k];
-  return wave_sum(acc);
+__device__ inline double seq_dot(const double* __restrict__ a, const double* __restrict__ b, int n) {
+#pragma clang fp contract(off)
+  double s = 0.0;
+  for (int k = 0; k < n; ++k) s = s + a[k] * b[k];
+  return s;
 }
 
 // Fingerprint + retrieval, one wave64.  Entries fill the bank in slot order
-// (id -1 = empty).
+// (id -1 = empty).  lds: (kMaxBank + 1) doubles of scores, then fp_dim doubles
+// of the raw fingerprint.
 __global__ __launch_bounds__(64) void retrieve_kernel(const float* __restrict__ fp_raw,
                                                       double* __restrict__ phi_cur,
                                                       const double* __restrict__ bank_phi,
                                                       DevState* __restrict__ st, int fp_dim,
                                                       const BankRule rule, int block,
                                                       int32_t* slot_out) {
+  extern __shared__ double lds[];
+  double* const score = lds;
+  double* const x = lds + kMaxBank + 1;
   const int lane = threadIdx.x;
-  // phi_b = x / ||x||_2, zero stays zero
-  double ss = 0.0;
-  for (int k = lane; k < fp_dim; k += 64) {
-    const double x = (double)fp_raw[k];
-    ss += x * x;
-  }
-  const double nrm = sqrt(wave_sum(ss));
-  for (int k = lane; k < fp_dim; k += 64) {
-    const double x = (double)fp_raw[k];
-    phi_cur[k] = nrm > 0.0 ? x / nrm : 0.0;
-  }
-  __syncthreads();  // phi_cur is re-read below by other lanes
+  for (int k = lane; k < fp_dim; k += 64) x[k] = (double)fp_raw[k];
+  __syncthreads();
+  // ||x||^2 as an index-order sum (every lane computes the same value), the
+  // correctly rounded square root, one correctly rounded division per
+  // element; zero stays zero
+  const double ss = seq_dot(x, x, fp_dim);
+  const double nrm = sqrt(ss);
+  for (int k = lane; k < fp_dim; k += 64) phi_cur[k] = nrm > 0.0 ? x[k] / nrm : 0.0;
+  __syncthreads();  // phi_cur is read back below by other lanes
+  // score of entry s by lane s
+  if (lane < rule.size && st->ids[lane] >= 0) score[lane] = seq_dot(phi_cur, bank_phi + (size_t)lane * fp_dim, fp_dim);
+  __syncthreads();
+  if (lane != 0) return;
   // r(b) = argmax over entries whose id != b-1; strict '>' keeps the lowest
   // slot on ties.  best: over every entry (the gated refresh's distance).
   const bool undetected = nrm == 0.0 && (rule.policy & kBankZeroFallback);
@@ -223,19 +225,18 @@ __global__ __launch_bounds__(64) void retrieve_kernel(const float* __restrict__ 
   double best_r = 0.0, best = -INFINITY;
   for (int s = 0; s < rule.size; ++s) {
     if (st->ids[s] < 0) continue;
-    const double sc = dot_f64(phi_cur, bank_phi + (size_t)s * fp_dim, fp_dim, lane);
+    const double sc = score[s];
     best = fmax(best, sc);
     if (st->ids[s] == block - 1 || undetected) continue;
     if (r < 0 || sc > best_r) { r = s; best_r = sc; }
   }
-  if (lane == 0) {  // the Dynamic Sink of this block is bank entry r (none if r < 0)
-    st->last_r = r;
-    st->dyn_id = r >= 0 ? st->ids[r] : -1;
-    if (r >= 0) st->last_used[r] = block;
-    st->phi_zero = nrm == 0.0;
-    st->best = best;
-    if (slot_out) *slot_out = r;
-  }
+  // the Dynamic Sink of this block is bank entry r (none if r < 0)
+  st->last_r = r;
+  st->dyn_id = r >= 0 ? st->ids[r] : -1;
+  if (r >= 0) st->last_used[r] = block;
+  st->phi_zero = nrm == 0.0;
+  st->best = best;
+  if (slot_out) *slot_out = r;
 }
 
 // Diversity bank update, one wave64.  The fill phase (block < fill_blocks)
@@ -248,6 +249,7 @@ __global__ __launch_bounds__(64) void bank_update_kernel(const double* __restric
                                                          DevState* __restrict__ st, int fp_dim,
                                                          const BankRule rule, int block,
                                                          int win_slot, int bank_slot0) {
+#pragma clang fp contract(off)
   const int lane = threadIdx.x;
   const int M = rule.size;
   int count = 0;
@@ -262,21 +264,23 @@ __global__ __launch_bounds__(64) void bank_update_kernel(const double* __restric
   } else {
     __shared__ double G[kMaxBank][kMaxBank];  // pairwise dots of the bank, i < j
     __shared__ double g[kMaxBank];            // dots with the candidate
-    for (int i = 0; i < M; ++i) {
-      const double gi = dot_f64(phi_cur, bank_phi + (size_t)i * fp_dim, fp_dim, lane);
-      if (lane == 0) g[i] = gi;
-      for (int j = i + 1; j < M; ++j) {
-        const double gij = dot_f64(bank_phi + (size_t)i * fp_dim, bank_phi + (size_t)j * fp_dim,
-                                   fp_dim, lane);
-        if (lane == 0) G[i][j] = gij;
-      }
+    // one lane per dot product: lanes 0..M-1 the candidate against entry i,
+    // the next M(M-1)/2 lanes the pairs (i, j), i < j, in lexicographic order
+    // (at most 8 + 28 < 64 lanes)
+    if (lane < M) {
+      g[lane] = seq_dot(phi_cur, bank_phi + (size_t)lane * fp_dim, fp_dim);
+    } else {
+      int t = lane - M;
+      for (int i = 0; i < M; ++i)
+        for (int j = i + 1; j < M; ++j, --t)
+          if (t == 0) G[i][j] = seq_dot(bank_phi + (size_t)i * fp_dim, bank_phi + (size_t)j * fp_dim, fp_dim);
     }
     __syncthreads();
     const double npairs = (double)(M * (M - 1) / 2);
     // mean pairwise similarity of an option, summed over pairs in slot order
     double tot = 0.0;
     for (int i = 0; i < M; ++i)
-      for (int j = i + 1; j < M; ++j) tot += G[i][j];
+      for (int j = i + 1; j < M; ++j) tot = tot + G[i][j];
     double best = tot / npairs;
     dec = -1;
     for (int x = 0; x < M; ++x) {
@@ -285,7 +289,7 @@ __global__ __launch_bounds__(64) void bank_update_kernel(const double* __restric
       if (!evictable) continue;
       double t = 0.0;
       for (int i = 0; i < M; ++i)
-        for (int j = i + 1; j < M; ++j) t += (i == x) ? g[j] : (j == x) ? g[i] : G[i][j];
+        for (int j = i + 1; j < M; ++j) t = t + ((i == x) ? g[j] : (j == x) ? g[i] : G[i][j]);
       const double sx = t / npairs;
       if (sx < best) { best = sx; dec = x; }
     }
@@ -368,7 +372,8 @@ hipError_t launch_slot_copy(char* block_base, size_t slot_bytes, size_t copy_byt
 hipError_t launch_retrieve(const float* fp_raw, double* phi_cur, const double* bank_phi,
                            DevState* st, int fp_dim, const BankRule& rule, int block, int32_t* slot_out,
                            hipStream_t s) {
-  hipLaunchKernelGGL(retrieve_kernel, dim3(1), dim3(64), 0, s, fp_raw, phi_cur, bank_phi, st,
+  const size_t lds = sizeof(double) * ((size_t)kMaxBank + 1 + (size_t)fp_dim);
+  hipLaunchKernelGGL(retrieve_kernel, dim3(1), dim3(64), lds, s, fp_raw, phi_cur, bank_phi, st,
                      fp_dim, rule, block, slot_out);
   return hipGetLastError();
 }
