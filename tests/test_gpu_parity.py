@@ -1,9 +1,9 @@
 """GPU parity: the HIP path through the C ABI against the fp64 oracle.
 
-Integer / byte results (retrieved slot, bank ids, stored K/V bytes) must match
-exactly; attention matches to rel-L2 <= 1e-2 and max-abs <= 3e-2 in bf16 and
-to 1e-5 in fp32; bank fingerprints match to 1e-14 (fp64, different summation
-order).
+Integer / byte results (retrieved slot, bank ids, stored K/V bytes) and the
+bank fingerprints (fp64 bits: both sides add every dot product in index
+order) must match exactly; attention matches to rel-L2 <= 1e-2 and max-abs
+<= 3e-2 in bf16 and to 1e-5 in fp32.
 """
 import math
 import sys
@@ -34,6 +34,15 @@ def to_dev(a, dtype):
 
 def rel_l2(a, b):
     return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300))
+
+
+def assert_phi_bits(got, want, what):
+    """Bank fingerprints equal the oracle's bit for bit (fp64)."""
+    want = np.array(want, dtype=np.float64).reshape(len(want), -1)
+    got = np.ascontiguousarray(got, dtype=np.float64)
+    assert got.shape == want.shape, f"{what}: bank shape"
+    diff = got.view(np.uint64) != want.view(np.uint64)
+    assert not diff.any(), f"{what}: {int(diff.sum())} fingerprint values differ in their bits"
 
 
 def check_attn(out, ref, cfg, what):
@@ -127,8 +136,7 @@ class Stream:
         ids, phi, misc = self.cache.bank_state()
         n = len(self.orc.bank_ids)
         assert list(ids[:n]) == self.orc.bank_ids and all(ids[n:] == -1), f"block {b}: bank ids"
-        for i in range(n):
-            np.testing.assert_allclose(phi[i], self.orc.bank_phi[i], rtol=0, atol=1e-14)
+        assert_phi_bits(phi[:n], self.orc.bank_phi, f"block {b}")
         if dec is not None:
             kind, slot = dec
             expect = slot if kind in ("insert", "swap") else -1
@@ -139,6 +147,18 @@ class Stream:
         return check_rotations(self.cache, self.orc, self.cfg, layer,
                                synth.ref_kv(self.cfg, layer, self.seed)[0],
                                lambda bid: self.clean(bid, layer)[0])
+
+    def check_ref_bytes(self, layer):
+        """The raw Ref Sink K/V of a layer equal the tensors set_ref got, bit for
+        bit; padding rows are zero."""
+        kt, vt = self.cache.slot_view(binding.SLOT_REF, layer)
+        k, v = synth.ref_kv(self.cfg, layer, self.seed)
+        T = self.cfg.ref_tokens
+        bits = torch.int16 if self.dt == torch.bfloat16 else torch.int32
+        for got, src in ((kt.cpu(), k), (vt.cpu(), v)):
+            want = torch.from_numpy(np.ascontiguousarray(src)).to(self.dt)
+            assert torch.equal(got[:T].contiguous().view(bits), want.view(bits)), f"Ref layer {layer}"
+            assert not got[T:].any()
 
     def check_slot_bytes(self, slot, block, layer):
         """Stored raw K/V of a slot equal the block's clean K/V bit for bit; padding is zero."""
@@ -167,7 +187,9 @@ def test_c0_stream_30_blocks_fp32():
             worst = max(worst, st.attend_check(l, step=b % 3))
         st.close(b)
     log(f"C0 worst rel-L2 {worst:.3g}")
-    # stored bytes: bank entries, Static, the window
+    # stored bytes: the Ref Sink, bank entries, Static, the window
+    for l in range(cfg.n_layers):
+        st.check_ref_bytes(l)
     for i, bid in enumerate(st.orc.bank_ids):
         for l in range(cfg.n_layers):
             st.check_slot_bytes(st.cache.slot_index_bank(i), bid, l)
@@ -199,6 +221,8 @@ def test_bf16_multitile_every_block(cfg):
         st.close(b)
     for i, bid in enumerate(st.orc.bank_ids):
         st.check_slot_bytes(st.cache.slot_index_bank(i), bid, 1)
+    for l in range(cfg.n_layers):
+        st.check_ref_bytes(l)
 
 
 @pytest.mark.parametrize("window,bank,dtype", [
@@ -270,12 +294,15 @@ def _oracle_to(cfg, n_blocks, fps):
     return orc
 
 
+@pytest.mark.timeout(900)
 @pytest.mark.parametrize("name,cfg,b,seed", [
     ("C1_480x480", synth.C1_480.replace(n_layers=1), 25, 1),
     ("C2_384x672_slid7", synth.C2_384x672.replace(n_layers=1), 32, 2),
 ])
-def test_full_size_sampled_parity(name, cfg, b, seed):
-    """Full-size call in the benchmark's launch configuration; sampled rows/heads vs oracle."""
+def test_full_size_whole_output_parity(name, cfg, b, seed):
+    """Full-size call in the benchmark's launch configuration: every query row of every
+    head (all 8 XCD groups of heads) against the oracle, element by element; the same call
+    again is bitwise identical; RoPE follow after the window has slid."""
     log(f"case: {name} full size, block {b}, seed {seed}")
     fps = synth.pose_stream(b + 1, seed=seed)
     kv_of = lambda blk, l: synth.clean_kv_torch(cfg, blk, l, seed, DEV)
@@ -287,21 +314,31 @@ def test_full_size_sampled_parity(name, cfg, b, seed):
     out = cache.attend(0, q, kc, vc)
     torch.cuda.synchronize()
     assert torch.isfinite(out).all()
-    T = cfg.block_tokens
-    rows = sorted({0, 1, 31, 32, 127, 128, 129, 255, 256, 1000, T // 2, T - 129, T - 65, T - 2, T - 1})
-    heads = [0, 7, 17, cfg.n_heads - 1]
-    host = lambda t: t.float().cpu().numpy()
-    ref = orc.attend(host(q), host(kc), host(vc),
-                     tuple(host(x) for x in synth.ref_kv_torch(cfg, 0, seed, DEV)),
-                     lambda bid: tuple(host(x) for x in kv_of(bid, 0)), q_rows=rows, heads=heads)
-    got = host(out)[rows][:, heads]
-    err = check_attn(got, ref, cfg, name)
-    log(f"{name}: sampled rel-L2 {err:.3g}")
     # same call again: bitwise identical
     out2 = cache.attend(0, q, kc, vc)
     assert torch.equal(out, out2)
+    host = lambda t: t.float().cpu().numpy()
+    got = host(out)
+    qh, kh, vh = host(q), host(kc), host(vc)
+    ref_h = tuple(host(x) for x in synth.ref_kv_torch(cfg, 0, seed, DEV))
+    block_h = {}
+
+    def block_kv(bid):
+        if bid not in block_h:
+            block_h[bid] = tuple(host(x) for x in kv_of(bid, 0))
+        return block_h[bid]
+
+    ref = np.empty_like(got)
+    for h in range(cfg.n_heads):  # one head at a time keeps the fp64 scores to a few hundred MB
+        ref[:, h:h + 1] = orc.attend(qh, kh, vh, ref_h, block_kv, heads=[h])
+        if h % 10 == 9:
+            log(f"{name}: oracle heads 0..{h} done")
+    err = check_attn(got, ref, cfg, name)
+    per_head = [rel_l2(got[:, h], ref[:, h]) for h in range(cfg.n_heads)]
+    log(f"{name}: whole output ({cfg.block_tokens} x {cfg.n_heads} x {cfg.head_dim}) rel-L2 {err:.3g}, "
+        f"worst head {max(per_head):.3g}, max-abs {float(np.abs(got - ref).max()):.3g}")
     # RoPE follow after the window has slid: window blocks and the Dynamic Sink
-    n = check_rotations(cache, orc, cfg, 0, None, lambda bid: host(kv_of(bid, 0)[0]),
+    n = check_rotations(cache, orc, cfg, 0, None, lambda bid: block_kv(bid)[0],
                         kinds=(O.SEG_WINDOW, O.SEG_DYNAMIC))
     assert n == 3
 
@@ -496,13 +533,13 @@ def test_bank_policies_every_block():
     fps = np.concatenate([synth.pose_stream(20, n_protos=6, seed=5),
                           synth.pose_stream(20, n_protos=6, seed=77)])
     fps[[3, 23, 24, 31]] = 0.0
-    # the gate must not sit within rounding of any block's best dot product
-    # (the device sums its fp64 dots in another order): check on the oracle
+    # every branch is exercised (checked on the oracle); the device adds its
+    # fp64 dot products in the oracle's order, so the gate and every decision
+    # agree whatever the distance to tau
     probe = O.PRSinkOracle(cfg)
     branches = set()
     for b in range(40):
         probe.open_block(b, fps[b])
-        assert not abs(probe.best_score - cfg.bank_refresh_tau) < 1e-9
         gate = probe.best_score < cfg.bank_refresh_tau
         dec = probe.close_block(b)
         if b >= cfg.bank_fill_blocks and dec and dec[0] == "swap":
