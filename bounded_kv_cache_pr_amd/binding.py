@@ -121,6 +121,7 @@ class PRSinkCache:
         self.nbytes = arena_bytes(cfg)
         self.dry_run = dry_run
         self._h = c_void_p()
+        self._attend_events = None  # kept alive while the library records them
         if dry_run:
             self.arena = None
             check(lib().pr_sink_cache_init(byref(self._c), None, 0, None, byref(self._h)))
@@ -206,10 +207,21 @@ class PRSinkCache:
         return ids, phi, tuple(int(x) for x in misc)
 
     def set_attend_events(self, start=None, stop=None):
-        """Records torch.cuda.Events (timing enabled, already created) around
-        every later attention kernel; no arguments turns it off."""
-        h = (lambda e: c_void_p(e.cuda_event) if e is not None else None)
-        check(lib().pr_sink_set_attend_events(self._h, h(start), h(stop)))
+        """Records torch.cuda.Events (timing enabled, already created, i.e.
+        recorded once) around every later attention kernel; no arguments turns
+        it off.  The cache keeps the two events alive while they are in use."""
+        if (start is None) != (stop is None):
+            raise ValueError("set both events or neither")
+        if start is not None:
+            for e in (start, stop):
+                if not e.cuda_event:
+                    raise ValueError("event has no HIP event yet: record it once before handing it over")
+            check(lib().pr_sink_set_attend_events(self._h, c_void_p(start.cuda_event),
+                                                  c_void_p(stop.cuda_event)))
+            self._attend_events = (start, stop)
+        else:
+            check(lib().pr_sink_set_attend_events(self._h, None, None))
+            self._attend_events = None
 
     def segments(self):
         """[(tokens, t_start)] of the open block in cache order."""

@@ -29,7 +29,7 @@
 //   * Ragged tiles (the last of each segment) run afterwards through the exact
 //     online-softmax step with masking; tile order does not change the result.
 // The fp32 kernel is a plain one-query-per-lane loop for fp32 caches.
-#include "prsink_internal.h"
+#include "prsink_device.h"
 
 #include <type_traits>
 

@@ -226,7 +226,7 @@ struct pr_sink_cache {
     hipStream_t seen = nullptr;   // (the null stream is a stream too)
   };
   std::vector<Mark> clean;  // per layer: the last clean write of that layer
-  Mark ref;                 // the last Ref Sink write
+  std::vector<Mark> ref;    // per layer: the last Ref Sink write of that layer
   Mark attn;                // the last attention call
   Mark retr;                // the last retrieval
   Mark dec;                 // the last bank decision (state only; entries may still be copying)
@@ -237,7 +237,8 @@ struct pr_sink_cache {
   ~pr_sink_cache() {
     auto drop = [](Mark& m) { if (m.ev) (void)hipEventDestroy(m.ev); };
     for (Mark& m : clean) drop(m);
-    drop(ref); drop(attn); drop(retr); drop(dec); drop(bank); drop(done[0]); drop(done[1]);
+    for (Mark& m : ref) drop(m);
+    drop(attn); drop(retr); drop(dec); drop(bank); drop(done[0]); drop(done[1]);
   }
 
   char* block_slot(int bs) const { return arena + lay.off_blocks + (size_t)bs * lay.slot_b; }
@@ -439,6 +440,7 @@ int cache_init(const pr_sink_config* cfg, void* arena_dev, size_t arena_bytes, v
   c->n_cu = n_cu;
   try {
     c->clean.resize(cfg->n_layers);
+    c->ref.resize(cfg->n_layers);
   } catch (...) {
     delete c;
     throw;
@@ -447,7 +449,8 @@ int cache_init(const pr_sink_config* cfg, void* arena_dev, size_t arena_bytes, v
     auto make = [](pr_sink_cache::Mark& m) { return hipEventCreateWithFlags(&m.ev, hipEventDisableTiming); };
     hipError_t e = hipSuccess;
     for (auto& m : c->clean) if (e == hipSuccess) e = make(m);
-    for (auto* m : {&c->ref, &c->attn, &c->retr, &c->dec, &c->bank, &c->done[0], &c->done[1]})
+    for (auto& m : c->ref) if (e == hipSuccess) e = make(m);
+    for (auto* m : {&c->attn, &c->retr, &c->dec, &c->bank, &c->done[0], &c->done[1]})
       if (e == hipSuccess) e = make(*m);
     if (e != hipSuccess) {
       delete c;
@@ -477,14 +480,17 @@ int pr_sink_set_ref(pr_sink_cache* c, int32_t layer, const void* k_raw, const vo
     const Layout& L = c->lay;
     hipStream_t s = as_stream(stream);
     char* ref = c->ref_slot();
-    PRS_HIP(after(s, c->attn));  // earlier attention read the old Ref Sink
+    // earlier attention read the old Ref Sink; an earlier write of the same
+    // layer, possibly on another stream, must land first (write after write)
+    PRS_HIP(after(s, c->attn));
+    PRS_HIP(after(s, c->ref[layer]));
     PRS_HIP(launch_kv_write(k_raw, v_raw, ref + c->k_off(layer, L.kv_r), ref + c->v_off(layer, L.kv_r),
                             nullptr, nullptr, block_bytes(c, L.tr), s));
     // the Ref Sink's place never moves: rotate its keys once
     RotParams r = rot_params(c, L.tr, L.kv_r);
     add_job(r, ref + c->k_off(layer, L.kv_r), ref + c->r_off(layer, L.kv_r), 0);
     PRS_HIP(launch_rope_follow(r, 1, s));
-    PRS_HIP(mark(s, c->ref));
+    PRS_HIP(mark(s, c->ref[layer]));
   }
   c->ref_set[layer] = 1;
   return PR_SINK_OK;
@@ -549,11 +555,11 @@ int pr_sink_attend(pr_sink_cache* c, int32_t layer, const void* q_raw, const voi
   const int n_seg = g.window_slots + 3;
   hipStream_t st = as_stream(stream);
   // this layer's newest window block (the previous block's clean write), the
-  // retrieval, the Ref Sink, and the previous call (attention calls share the
-  // rotated-current-key scratch and the split-job records)
+  // retrieval, this layer's Ref Sink, and the previous call (attention calls
+  // share the rotated-current-key scratch and the split-job records)
   PRS_HIP(after(st, c->clean[layer]));
   PRS_HIP(after(st, c->retr));
-  PRS_HIP(after(st, c->ref));
+  PRS_HIP(after(st, c->ref[layer]));
   PRS_HIP(after(st, c->attn));
   // the current block's keys, rotated at the current positions
   char* cur_rot = c->arena + L.off_cur_rot;
