@@ -23,7 +23,7 @@ EXPORTED = (
     "pr_sink_arena_bytes", "pr_sink_cache_init", "pr_sink_set_ref", "pr_sink_retrieve",
     "pr_sink_attend", "pr_sink_clean_kv_write", "pr_sink_bank_update", "pr_sink_bank_state",
     "pr_sink_slot_view", "pr_sink_segments", "pr_sink_set_attend_events", "pr_sink_cache_destroy",
-    "pr_sink_last_error",
+    "pr_sink_last_error", "pr_sink_attend_noalloc",
 )
 
 
@@ -69,6 +69,7 @@ def lib() -> ctypes.CDLL:
             "pr_sink_set_ref": (i32, [vp, i32, vp, vp, vp]),
             "pr_sink_retrieve": (i32, [vp, i32, vp, vp, vp]),
             "pr_sink_attend": (i32, [vp, i32, vp, vp, vp, vp, vp]),
+            "pr_sink_attend_noalloc": (i32, [vp, i32, vp, vp, vp, vp, vp]),
             "pr_sink_clean_kv_write": (i32, [vp, i32, vp, vp, vp]),
             "pr_sink_bank_update": (i32, [vp, i32, vp]),
             "pr_sink_bank_state": (i32, [vp, vp, vp, vp, vp]),
@@ -186,6 +187,16 @@ class PRSinkCache:
         check(lib().pr_sink_attend(self._h, layer, self._ptr(q, n, "q"), self._ptr(k, n, "k"),
                                    self._ptr(v, n, "v"), self._ptr(out, n, "out"),
                                    self._stream()))
+        return out
+
+    def attend_noalloc(self, layer: int, q, k, v, out):
+        """pr_sink_attend_noalloc: the same attention call with its scratch in the
+        library's static device array (calls on one GPU must not overlap); the
+        caller passes the output tensor, nothing is allocated."""
+        n = self.cfg.block_tokens
+        check(lib().pr_sink_attend_noalloc(self._h, layer, self._ptr(q, n, "q"), self._ptr(k, n, "k"),
+                                           self._ptr(v, n, "v"), self._ptr(out, n, "out"),
+                                           self._stream()))
         return out
 
     def clean_kv_write(self, layer: int, k, v):

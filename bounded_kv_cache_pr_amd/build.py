@@ -12,7 +12,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB_DIR = os.path.join(PKG, "lib")
 LIB_PATH = os.path.join(LIB_DIR, "libprsink.so")
 
-SOURCES = ("prsink_host.cpp", "kernels_attn.hip", "kernels_cache.hip")
+SOURCES = ("prsink_host.cpp", "kernels_attn.hip", "kernels_cache.hip", "attend_noalloc.hip")
 ARCH = "gfx950"
 
 

@@ -540,6 +540,20 @@ int pr_sink_retrieve(pr_sink_cache* c, int32_t block, const float* fp_raw_dev,
 
 int pr_sink_attend(pr_sink_cache* c, int32_t layer, const void* q_raw, const void* k_cur_raw,
                    const void* v_cur_raw, void* out, void* stream) {
+  return prsink::attend_with_workspace(c, layer, q_raw, k_cur_raw, v_cur_raw, out, stream, nullptr);
+}
+
+}  // extern "C"
+
+bool prsink::cache_is_dry(const pr_sink_cache* c) { return c->dry; }
+
+int prsink::report_hip_error(hipError_t e, const char* what) {
+  return fail(PR_SINK_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// One attention call; ws == nullptr takes the per-call scratch from the arena.
+int prsink::attend_with_workspace(pr_sink_cache* c, int32_t layer, const void* q_raw, const void* k_cur_raw,
+                                  const void* v_cur_raw, void* out, void* stream, const AttendWorkspace* ws) {
   if (int e = check_layer(c, layer)) return e;
   if (int e = check_tensor(q_raw, "q_raw")) return e;
   if (int e = check_tensor(k_cur_raw, "k_cur_raw")) return e;
@@ -547,6 +561,9 @@ int pr_sink_attend(pr_sink_cache* c, int32_t layer, const void* q_raw, const voi
   if (int e = check_tensor(out, "out")) return e;
   if (out == q_raw || out == k_cur_raw || out == v_cur_raw) return fail(PR_SINK_EINVAL, "out aliases an input");
   if (!c->open) return fail(PR_SINK_ESTATE, "attend with no open block");
+  if (ws && block_bytes(c, c->lay.tb) > ws->cur_rot_bytes)
+    return fail(PR_SINK_EINVAL, "the current block's keys need %zu bytes of scratch, the workspace holds %zu",
+                block_bytes(c, c->lay.tb), ws->cur_rot_bytes);
   if (c->dry) return PR_SINK_OK;
   const pr_sink_config& g = c->cfg;
   const Layout& L = c->lay;
@@ -562,7 +579,7 @@ int pr_sink_attend(pr_sink_cache* c, int32_t layer, const void* q_raw, const voi
   PRS_HIP(after(st, c->ref[layer]));
   PRS_HIP(after(st, c->attn));
   // the current block's keys, rotated at the current positions
-  char* cur_rot = c->arena + L.off_cur_rot;
+  char* cur_rot = ws ? static_cast<char*>(ws->cur_rot) : c->arena + L.off_cur_rot;
   {
     RotParams r = rot_params(c, L.tb, 0);
     add_job(r, k_cur_raw, cur_rot, t_index[n_seg - 1]);
@@ -612,14 +629,17 @@ int pr_sink_attend(pr_sink_cache* c, int32_t layer, const void* q_raw, const voi
   p.q_t_index = t_index[n_seg - 1];
   p.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)g.head_dim));
   p.dyn_may_vanish = (g.bank_policy & PR_SINK_BANK_ZERO_FALLBACK) != 0;
-  p.part = L.n_part_rec ? reinterpret_cast<float*>(c->arena + L.off_part) : nullptr;
-  p.cnt = L.n_cnt ? reinterpret_cast<uint32_t*>(c->arena + L.off_cnt) : nullptr;
+  // a caller-provided workspace carries no split-job records: every job runs whole
+  p.part = L.n_part_rec && !ws ? reinterpret_cast<float*>(c->arena + L.off_part) : nullptr;
+  p.cnt = L.n_cnt && !ws ? reinterpret_cast<uint32_t*>(c->arena + L.off_cnt) : nullptr;
   if (c->time_start) PRS_HIP(hipEventRecord(c->time_start, st));
   PRS_HIP(launch_attention(p, g.dtype, g.head_dim, c->n_cu, st));
   if (c->time_stop) PRS_HIP(hipEventRecord(c->time_stop, st));
   PRS_HIP(mark(st, c->attn));
   return PR_SINK_OK;
 }
+
+extern "C" {
 
 int pr_sink_clean_kv_write(pr_sink_cache* c, int32_t layer, const void* k_raw, const void* v_raw,
                            void* stream) {

@@ -164,4 +164,25 @@ hipError_t launch_bank_update(const double* phi_cur, double* bank_phi, DevState*
                               int win_slot, int bank_slot0, hipStream_t s);
 hipError_t launch_state_init(DevState* st, hipStream_t s);
 
+// Per-call scratch of an attention call supplied by the caller of
+// attend_with_workspace instead of the arena: cur_rot receives the current
+// block's rotated keys (cur_rot_bytes available).  Such a call plans no
+// split jobs, so it needs no partial records or counters.
+struct AttendWorkspace {
+  void* cur_rot;
+  size_t cur_rot_bytes;
+};
+
+}  // namespace prsink
+
+struct pr_sink_cache;
+namespace prsink {
+// True for a dry-run cache (no arena, no device).
+bool cache_is_dry(const pr_sink_cache* c);
+// Records a HIP failure as the calling thread's last error; returns PR_SINK_EHIP.
+int report_hip_error(hipError_t e, const char* what);
+// pr_sink_attend with its per-call scratch taken from ws (nullptr: the arena).
+int attend_with_workspace(pr_sink_cache* c, int32_t layer, const void* q_raw, const void* k_cur_raw,
+                          const void* v_cur_raw, void* out, void* stream, const AttendWorkspace* ws);
+
 }  // namespace prsink

@@ -198,6 +198,20 @@ int pr_sink_retrieve(pr_sink_cache* c, int32_t block, const float* fp_raw_dev,
 int pr_sink_attend(pr_sink_cache* c, int32_t layer, const void* q_raw, const void* k_cur_raw,
                    const void* v_cur_raw, void* out, void* stream);
 
+/* pr_sink_attend for callers that cannot allocate device memory or hand the
+ * library a workspace (code under stream capture, tight serving loops): the
+ * same call, except that the current block's rotated keys go to a static
+ * device array of this library (64 MiB per GPU the library runs on, held
+ * until the process ends) instead of the arena, and every attention job runs
+ * whole (no split partial results).  Allocates nothing.  Returns
+ * PR_SINK_EINVAL, leaving the cache unchanged, when the current block's keys
+ * (block tokens x n_heads x head_dim x element size) exceed 64 MiB.  All calls
+ * of this entry point on one GPU share the array: calls that may overlap on
+ * one GPU (other streams, other caches, other threads) race and must not be
+ * issued; each call overwrites what the previous one left there. */
+int pr_sink_attend_noalloc(pr_sink_cache* c, int32_t layer, const void* q_raw, const void* k_cur_raw,
+                           const void* v_cur_raw, void* out, void* stream);
+
 /* Clean KV Update, write half: stores the clean raw K/V of the open block for
  * `layer` (device, [T][H][d]) into its rolling-window slot, and for block 0
  * also into the Static Sink (review, full-pipeline paragraph; HF abstract:

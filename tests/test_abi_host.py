@@ -141,6 +141,32 @@ def test_argument_validation():
     assert _code(c.attend, 0, FAKE, FAKE + 16, FAKE + 32, FAKE) == PR_SINK_EINVAL  # out aliases q
 
 
+def test_attend_noalloc_validates_like_attend_and_rejects_blocks_over_64_mib():
+    """pr_sink_attend_noalloc takes the same arguments and call order as
+    pr_sink_attend; a block whose rotated keys exceed the 64 MiB static scratch
+    is rejected with PR_SINK_EINVAL before anything is queued."""
+    cfg = synth.C0_TINY
+    c = _dry(cfg)
+    assert _code(c.attend_noalloc, 0, FAKE, FAKE + 16, FAKE + 32, FAKE + 48) == PR_SINK_ESTATE
+    for l in range(cfg.n_layers):
+        c.set_ref(l, FAKE, FAKE)
+    c.retrieve(0, FAKE)
+    c.attend_noalloc(0, FAKE, FAKE + 16, FAKE + 32, FAKE + 48)
+    assert _code(c.attend_noalloc, 0, FAKE, FAKE + 16, FAKE + 32, FAKE) == PR_SINK_EINVAL  # out aliases q
+    assert _code(c.attend_noalloc, 5, FAKE, FAKE + 16, FAKE + 32, FAKE + 48) == PR_SINK_EINVAL
+    # 3 frames x 64 x 64 tokens x 64 heads x 128 dims x 2 bytes = 192 MiB of keys
+    big = synth.C1_480.replace(n_layers=1, n_heads=64, lat_h=64, lat_w=64)
+    c = _dry(big)
+    c.set_ref(0, FAKE, FAKE)
+    c.retrieve(0, FAKE)
+    c.attend(0, FAKE, FAKE + 16, FAKE + 32, FAKE + 48)  # the arena-backed call has room
+    assert _code(c.attend_noalloc, 0, FAKE, FAKE + 16, FAKE + 32, FAKE + 48) == PR_SINK_EINVAL
+    assert "64 MiB" in binding.last_error() or "scratch" in binding.last_error()
+    # the failed call left the block open and unchanged
+    c.clean_kv_write(0, FAKE, FAKE)
+    c.bank_update(0)
+
+
 def test_segment_layout_follows_the_block_protocol():
     cfg = synth.C0_TINY.replace(t0=3)
     c = _dry(cfg)
