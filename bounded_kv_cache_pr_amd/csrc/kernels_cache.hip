@@ -80,10 +80,11 @@ __global__ __launch_bounds__(256) void slot_copy_kernel(uint8_t* __restrict__ ba
 // on every call (clean_write rotates the window and Static places) (review on
 // paper.rainbus.top, full-pipeline paragraph: raw keys re-rotated at their
 // current cache positions; novelty paragraph: position-consistent reuse).
-// Pair (x0, x1) of a band at angle a becomes (x0 cos a - x1 sin a,
-// x0 sin a + x1 cos a), in fp32, rounded once to the cache dtype.
-// Thread = one 16-byte chunk (4 bf16 pairs or 2 fp32 pairs) of one token and
-// head; grid = (chunks, layer, job).
+// Pair (x0, x1) at angle a becomes (x0 cos a - x1 sin a, x0 sin a + x1 cos a),
+// in fp32, rounded once to the cache dtype; cos a and sin a come from the
+// place's [token][pair] table, one 32-byte (bf16) or 16-byte (fp32) read per
+// 16-byte chunk.  Thread = one 16-byte chunk (4 bf16 pairs or 2 fp32 pairs) of
+// one token and head; grid = (chunks, layer, job).
 // ---------------------------------------------------------------------------
 __device__ inline float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ inline float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
@@ -93,26 +94,35 @@ __device__ inline uint32_t pack_bf16(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
-// Chunk c (16 bytes: 4 bf16 pairs or 2 fp32 pairs) of one head row of a key
-// at position (tt, y, x), rotated.
-__device__ inline uint4 rotate_chunk(const RopeGeom& g, uint4 w, uint32_t c, int elem, int tt, int y, int x) {
+// Token of chunk i and the chunk's first RoPE pair within the head.
+__device__ __forceinline__ void chunk_place(const ChunkDiv& d, uint32_t i, int elem, uint32_t& n, uint32_t& pair) {
+  n = d.exact ? __umulhi(i, d.magic) : i / d.per_tok;
+  const uint32_t per_head = (uint32_t)d.np * 4 / 16 * (elem == 2 ? 1 : 2);  // chunks per head row (a power of 2)
+  pair = (i & (per_head - 1)) * (elem == 2 ? 4 : 2);
+}
+
+// Chunk w of a head row rotated with the table entries at cs (4 pairs in bf16,
+// 2 in fp32).
+__device__ __forceinline__ uint4 rotate_chunk(uint4 w, const float2* __restrict__ cs, int elem) {
   if (elem == 2) {
+    const float4 c01 = *reinterpret_cast<const float4*>(cs), c23 = *reinterpret_cast<const float4*>(cs + 2);
+    const float cx[4] = {c01.x, c01.z, c23.x, c23.z}, sx[4] = {c01.y, c01.w, c23.y, c23.w};
     uint32_t ws[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const float2 cs = rope_cs(g, (int)c * 4 + e, tt, y, x);
       const float x0 = bf16_lo(ws[e]), x1 = bf16_hi(ws[e]);
-      ws[e] = pack_bf16(x0 * cs.x - x1 * cs.y, x0 * cs.y + x1 * cs.x);
+      ws[e] = pack_bf16(x0 * cx[e] - x1 * sx[e], x0 * sx[e] + x1 * cx[e]);
     }
     return make_uint4(ws[0], ws[1], ws[2], ws[3]);
   }
+  const float4 c01 = *reinterpret_cast<const float4*>(cs);
+  const float cx[2] = {c01.x, c01.z}, sx[2] = {c01.y, c01.w};
   float f[4] = {__uint_as_float(w.x), __uint_as_float(w.y), __uint_as_float(w.z), __uint_as_float(w.w)};
 #pragma unroll
   for (int e = 0; e < 2; ++e) {
-    const float2 cs = rope_cs(g, (int)c * 2 + e, tt, y, x);
     const float x0 = f[2 * e], x1 = f[2 * e + 1];
-    f[2 * e] = x0 * cs.x - x1 * cs.y;
-    f[2 * e + 1] = x0 * cs.y + x1 * cs.x;
+    f[2 * e] = x0 * cx[e] - x1 * sx[e];
+    f[2 * e + 1] = x0 * sx[e] + x1 * cx[e];
   }
   return make_uint4(__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]), __float_as_uint(f[3]));
 }
@@ -129,16 +139,13 @@ __global__ __launch_bounds__(256) void rope_follow_kernel(const RotParams p) {
   } else {
     dst = jb.dst + lay;
   }
-  const uint32_t per_head = (uint32_t)(p.head_dim * p.elem / 16);  // chunks per head row
-  const uint32_t per_tok = per_head * (uint32_t)p.n_heads;
-  const uint32_t total = per_tok * (uint32_t)p.n_tok;
+  const uint32_t total = p.cd.per_tok * (uint32_t)p.n_tok;
   const uint32_t stride = gridDim.x * 256;
   for (uint32_t i = blockIdx.x * 256 + threadIdx.x; i < total; i += stride) {
-    const uint32_t n = i / per_tok;
-    const uint32_t c = (i - n * per_tok) % per_head;
-    int tt, y, x;
-    token_pos(p.g, (int)n, jb.t_index, tt, y, x);
-    reinterpret_cast<uint4*>(dst)[i] = rotate_chunk(p.g, reinterpret_cast<const uint4*>(src)[i], c, p.elem, tt, y, x);
+    const uint4 w = reinterpret_cast<const uint4*>(src)[i];
+    uint32_t n, pair;
+    chunk_place(p.cd, i, p.elem, n, pair);
+    reinterpret_cast<uint4*>(dst)[i] = rotate_chunk(w, jb.cs + (size_t)n * p.cd.np + pair, p.elem);
   }
 }
 
@@ -151,16 +158,15 @@ __global__ __launch_bounds__(256) void rope_follow_kernel(const RotParams p) {
 // window slides.  Thread = one 16-byte chunk of K and of V.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void clean_write_kernel(const CleanWrite p) {
-  const uint32_t per_head = (uint32_t)(p.head_dim * p.elem / 16);
-  const uint32_t per_tok = per_head * (uint32_t)p.n_heads;
-  const uint32_t total = per_tok * (uint32_t)p.n_tok;
+  const uint32_t total = p.cd.per_tok * (uint32_t)p.n_tok;
   const uint32_t stride = gridDim.x * 256;
   const uint4* __restrict__ ks = reinterpret_cast<const uint4*>(p.k_src);
   const uint4* __restrict__ vs = reinterpret_cast<const uint4*>(p.v_src);
   for (uint32_t i = blockIdx.x * 256 + threadIdx.x; i < total; i += stride) {
-    const uint32_t n = i / per_tok;
-    const uint32_t c = (i - n * per_tok) % per_head;
     const uint4 k = ld_nt(ks + i), v = ld_nt(vs + i);
+    uint32_t n, pair;
+    chunk_place(p.cd, i, p.elem, n, pair);
+    const size_t e = (size_t)n * p.cd.np + pair;
 #pragma unroll
     for (int d = 0; d < 2; ++d) {
       const CleanDst& o = p.dst[d];
@@ -170,9 +176,7 @@ __global__ __launch_bounds__(256) void clean_write_kernel(const CleanWrite p) {
 #pragma unroll
       for (int r = 0; r < kMaxRot; ++r) {
         if (r >= o.n_rot) break;
-        int tt, y, x;
-        token_pos(p.g, (int)n, o.t_index[r], tt, y, x);
-        st_nt(reinterpret_cast<uint4*>(o.k_rot[r]) + i, rotate_chunk(p.g, k, c, p.elem, tt, y, x));
+        st_nt(reinterpret_cast<uint4*>(o.k_rot[r]) + i, rotate_chunk(k, o.cs[r] + e, p.elem));
       }
     }
   }
@@ -185,37 +189,103 @@ __global__ __launch_bounds__(256) void clean_write_kernel(const CleanWrite p) {
 // implementation that adds in the same order gets the same bits, and the
 // retrieval and bank decisions never depend on how a reduction was split.
 // ---------------------------------------------------------------------------
-__device__ inline double seq_dot(const double* __restrict__ a, const double* __restrict__ b, int n) {
+// The vectors stream through LDS in chunks of kChunk elements, staged by the
+// whole wave, so each lane's sequential sum reads LDS rather than waiting on a
+// global load per element; the order of the additions is unchanged.
+constexpr int kChunk = 256;
+constexpr int kPerLane = kChunk / 64;
+
+// Rows [0, n_rows) of `rows` (row i at rows + i * n), elements [k0, k0+len),
+// into lds (row i at lds + i * kChunk).  Every lane issues all its loads
+// before its first LDS store, so the loads overlap.
+__device__ __forceinline__ void stage_rows(double* __restrict__ lds, const double* __restrict__ rows, int n_rows,
+                                           size_t n, int k0, int len, int lane) {
+  double v[kMaxBank + 1][kPerLane];
+#pragma unroll
+  for (int i = 0; i < kMaxBank + 1; ++i)
+#pragma unroll
+    for (int e = 0; e < kPerLane; ++e) {
+      const int k = lane + 64 * e;
+      v[i][e] = i < n_rows && k < len ? rows[(size_t)i * n + k0 + k] : 0.0;
+    }
+#pragma unroll
+  for (int i = 0; i < kMaxBank + 1; ++i)
+#pragma unroll
+    for (int e = 0; e < kPerLane; ++e) {
+      const int k = lane + 64 * e;
+      if (i < n_rows && k < len) lds[i * kChunk + k] = v[i][e];
+    }
+}
+
+// acc + x[0] y[0] + x[1] y[1] + ... + x[len-1] y[len-1], added one by one in
+// that order; eight elements are read (and multiplied) ahead of their adds.
+__device__ __forceinline__ double seq_dot_acc(double acc, const double* __restrict__ x, const double* __restrict__ y,
+                                              int len) {
 #pragma clang fp contract(off)
-  double s = 0.0;
-  for (int k = 0; k < n; ++k) s = s + a[k] * b[k];
-  return s;
+  int k = 0;
+  for (; k + 8 <= len; k += 8) {
+    double pr[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) pr[j] = x[k + j] * y[k + j];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc = acc + pr[j];
+  }
+  for (; k < len; ++k) acc = acc + x[k] * y[k];
+  return acc;
 }
 
 // Fingerprint + retrieval, one wave64.  Entries fill the bank in slot order
-// (id -1 = empty).  lds: (kMaxBank + 1) doubles of scores, then fp_dim doubles
-// of the raw fingerprint.
+// (id -1 = empty).
 __global__ __launch_bounds__(64) void retrieve_kernel(const float* __restrict__ fp_raw,
                                                       double* __restrict__ phi_cur,
                                                       const double* __restrict__ bank_phi,
                                                       DevState* __restrict__ st, int fp_dim,
                                                       const BankRule rule, int block,
                                                       int32_t* slot_out) {
-  extern __shared__ double lds[];
-  double* const score = lds;
-  double* const x = lds + kMaxBank + 1;
+#pragma clang fp contract(off)
+  __shared__ double lds[(kMaxBank + 1) * kChunk];
+  __shared__ double score[kMaxBank];
   const int lane = threadIdx.x;
-  for (int k = lane; k < fp_dim; k += 64) x[k] = (double)fp_raw[k];
-  __syncthreads();
-  // ||x||^2 as an index-order sum (every lane computes the same value), the
+  const int M = rule.size;
+  // ||x||^2 as an index-order sum (lane 0; the chunks go through LDS), the
   // correctly rounded square root, one correctly rounded division per
   // element; zero stays zero
-  const double ss = seq_dot(x, x, fp_dim);
+  double ss = 0.0;
+  for (int k0 = 0; k0 < fp_dim; k0 += kChunk) {
+    const int len = min(kChunk, fp_dim - k0);
+    float v[kPerLane];
+#pragma unroll
+    for (int e = 0; e < kPerLane; ++e) v[e] = lane + 64 * e < len ? fp_raw[k0 + lane + 64 * e] : 0.0f;
+#pragma unroll
+    for (int e = 0; e < kPerLane; ++e)
+      if (lane + 64 * e < len) lds[lane + 64 * e] = (double)v[e];
+    __syncthreads();
+    if (lane == 0) ss = seq_dot_acc(ss, lds, lds, len);
+    __syncthreads();
+  }
+  if (lane == 0) lds[0] = ss;
+  __syncthreads();
+  ss = lds[0];
+  __syncthreads();
   const double nrm = sqrt(ss);
-  for (int k = lane; k < fp_dim; k += 64) phi_cur[k] = nrm > 0.0 ? x[k] / nrm : 0.0;
+  for (int k = lane; k < fp_dim; k += 64) {
+    const double x = (double)fp_raw[k];
+    phi_cur[k] = nrm > 0.0 ? x / nrm : 0.0;
+  }
   __syncthreads();  // phi_cur is read back below by other lanes
-  // score of entry s by lane s
-  if (lane < rule.size && st->ids[lane] >= 0) score[lane] = seq_dot(phi_cur, bank_phi + (size_t)lane * fp_dim, fp_dim);
+  // score of entry s by lane s: phi_cur . phi_s, in index order (phi_cur
+  // staged as row M)
+  const bool active = lane < M && st->ids[lane] >= 0;
+  double acc = 0.0;
+  for (int k0 = 0; k0 < fp_dim; k0 += kChunk) {
+    const int len = min(kChunk, fp_dim - k0);
+    stage_rows(lds, bank_phi, M, fp_dim, k0, len, lane);
+    stage_rows(lds + M * kChunk, phi_cur, 1, fp_dim, k0, len, lane);
+    __syncthreads();
+    if (active) acc = seq_dot_acc(acc, lds + M * kChunk, lds + lane * kChunk, len);
+    __syncthreads();
+  }
+  if (active) score[lane] = acc;
   __syncthreads();
   if (lane != 0) return;
   // r(b) = argmax over entries whose id != b-1; strict '>' keeps the lowest
@@ -223,7 +293,7 @@ __global__ __launch_bounds__(64) void retrieve_kernel(const float* __restrict__ 
   const bool undetected = nrm == 0.0 && (rule.policy & kBankZeroFallback);
   int r = -1;
   double best_r = 0.0, best = -INFINITY;
-  for (int s = 0; s < rule.size; ++s) {
+  for (int s = 0; s < M; ++s) {
     if (st->ids[s] < 0) continue;
     const double sc = score[s];
     best = fmax(best, sc);
@@ -250,6 +320,9 @@ __global__ __launch_bounds__(64) void bank_update_kernel(const double* __restric
                                                          const BankRule rule, int block,
                                                          int win_slot, int bank_slot0) {
 #pragma clang fp contract(off)
+  __shared__ double lds[(kMaxBank + 1) * kChunk];
+  __shared__ double G[kMaxBank][kMaxBank];  // pairwise dots of the bank, i < j
+  __shared__ double g[kMaxBank];            // dots with the candidate
   const int lane = threadIdx.x;
   const int M = rule.size;
   int count = 0;
@@ -262,18 +335,38 @@ __global__ __launch_bounds__(64) void bank_update_kernel(const double* __restric
   } else if (count < M) {
     dec = count;
   } else {
-    __shared__ double G[kMaxBank][kMaxBank];  // pairwise dots of the bank, i < j
-    __shared__ double g[kMaxBank];            // dots with the candidate
-    // one lane per dot product: lanes 0..M-1 the candidate against entry i,
-    // the next M(M-1)/2 lanes the pairs (i, j), i < j, in lexicographic order
-    // (at most 8 + 28 < 64 lanes)
+    // one lane per dot product, each an index-order sum: lanes 0..M-1 the
+    // candidate (row M of the staged rows) against entry i, the next
+    // M(M-1)/2 lanes the pairs (i, j), i < j, in lexicographic order (at
+    // most 8 + 28 < 64 lanes)
+    int ia = 0, ib = 0;
+    bool active = true;
     if (lane < M) {
-      g[lane] = seq_dot(phi_cur, bank_phi + (size_t)lane * fp_dim, fp_dim);
+      ia = M;
+      ib = lane;
     } else {
       int t = lane - M;
+      active = false;
       for (int i = 0; i < M; ++i)
         for (int j = i + 1; j < M; ++j, --t)
-          if (t == 0) G[i][j] = seq_dot(bank_phi + (size_t)i * fp_dim, bank_phi + (size_t)j * fp_dim, fp_dim);
+          if (t == 0) {
+            ia = i;
+            ib = j;
+            active = true;
+          }
+    }
+    double acc = 0.0;
+    for (int k0 = 0; k0 < fp_dim; k0 += kChunk) {
+      const int len = min(kChunk, fp_dim - k0);
+      stage_rows(lds, bank_phi, M, fp_dim, k0, len, lane);
+      stage_rows(lds + M * kChunk, phi_cur, 1, fp_dim, k0, len, lane);
+      __syncthreads();
+      if (active) acc = seq_dot_acc(acc, lds + ia * kChunk, lds + ib * kChunk, len);
+      __syncthreads();
+    }
+    if (active) {
+      if (lane < M) g[lane] = acc;
+      else G[ia][ib] = acc;
     }
     __syncthreads();
     const double npairs = (double)(M * (M - 1) / 2);
@@ -372,8 +465,7 @@ hipError_t launch_slot_copy(char* block_base, size_t slot_bytes, size_t copy_byt
 hipError_t launch_retrieve(const float* fp_raw, double* phi_cur, const double* bank_phi,
                            DevState* st, int fp_dim, const BankRule& rule, int block, int32_t* slot_out,
                            hipStream_t s) {
-  const size_t lds = sizeof(double) * ((size_t)kMaxBank + 1 + (size_t)fp_dim);
-  hipLaunchKernelGGL(retrieve_kernel, dim3(1), dim3(64), lds, s, fp_raw, phi_cur, bank_phi, st,
+  hipLaunchKernelGGL(retrieve_kernel, dim3(1), dim3(64), 0, s, fp_raw, phi_cur, bank_phi, st,
                      fp_dim, rule, block, slot_out);
   return hipGetLastError();
 }

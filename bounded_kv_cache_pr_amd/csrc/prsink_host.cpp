@@ -74,11 +74,12 @@ struct Layout {
   int elem, tpf, tb, tr, tb_pad, tr_pad;
   size_t kv_b, slot_b;   // block slot: one tensor of one layer, whole slot
   size_t kv_r, slot_r;   // Ref slot
-  size_t off_state, off_phi_bank, off_phi_cur, off_rope, off_cur_rot, off_part, off_cnt, off_ref, off_blocks,
-      off_wrot, total;
+  size_t off_state, off_phi_bank, off_phi_cur, off_rope, off_ptab, off_cur_rot, off_part, off_cnt, off_ref,
+      off_blocks, off_wrot, total;
   size_t wrot_b;             // per window slot: its keys rotated at the older window places
   size_t n_part_rec, n_cnt;  // partial records and counters of split attention jobs
   int n_t, np_t, np_h, np_w, rope_h_off, rope_w_off, rope_entries;
+  size_t ptab_entries;  // per-place cos/sin: Ref [tr][np], then W + 2 block places [tb][np] each
   int n_block_slots;
 };
 
@@ -153,6 +154,11 @@ Layout make_layout(const pr_sink_config* c) {
   off = align_up(off + sizeof(double) * c->fp_dim, 256);
   L.off_rope = off;  // fp32 (cos, sin) table
   off = align_up(off + 8 * (size_t)L.rope_entries, kAlign);
+  // per-place tables for the rotation kernels: the Ref place, then the block
+  // places Static, Dynamic, the W-1 window places and the current block
+  L.off_ptab = off;
+  L.ptab_entries = ((size_t)L.tr + (size_t)(c->window_slots + 2) * L.tb) * (c->head_dim / 2);
+  off = align_up(off + 8 * L.ptab_entries, kAlign);
   L.off_cur_rot = off;
   off = align_up(off + L.kv_b, kAlign);
   // split attention jobs (bf16): per XCD fewer than kMaxCuPerXcd jobs are split,
@@ -198,6 +204,32 @@ std::vector<uint32_t> rope_table(const pr_sink_config* c, const Layout& L) {
   fill(0, L.n_t, c->t0, c->rope_dims[0]);
   fill(L.rope_h_off, c->lat_h, 0, c->rope_dims[1]);
   fill(L.rope_w_off, c->lat_w, 0, c->rope_dims[2]);
+  return t;
+}
+
+// The per-place tables, gathered from the band table: for a place whose first
+// frame has temporal row t_index, token n = (frame f, row y, column x) takes
+// the t band at row t_index + f, the h band at y and the w band at x.
+std::vector<uint32_t> place_tables(const pr_sink_config* c, const Layout& L, const std::vector<uint32_t>& band) {
+  const int np = c->head_dim / 2;
+  std::vector<uint32_t> t(2 * L.ptab_entries);
+  size_t e = 0;
+  auto place = [&](int t_index, int n_tok) {
+    for (int n = 0; n < n_tok; ++n) {
+      const int f = n / L.tpf, y = (n % L.tpf) / c->lat_w, x = n % c->lat_w;
+      for (int pr = 0; pr < np; ++pr) {
+        size_t b;
+        if (pr < L.np_t) b = (size_t)(t_index + f) * L.np_t + pr;
+        else if (pr < L.np_t + L.np_h) b = L.rope_h_off + (size_t)y * L.np_h + (pr - L.np_t);
+        else b = L.rope_w_off + (size_t)x * L.np_w + (pr - L.np_t - L.np_h);
+        t[2 * e] = band[2 * b];
+        t[2 * e + 1] = band[2 * b + 1];
+        ++e;
+      }
+    }
+  };
+  place(0, L.tr);
+  for (int k = 0; k < c->window_slots + 2; ++k) place(c->ref_frames + k * c->block_frames, L.tb);
   return t;
 }
 
@@ -251,6 +283,15 @@ struct pr_sink_cache {
   double* phi_bank() const { return reinterpret_cast<double*>(arena + lay.off_phi_bank); }
   double* phi_cur() const { return reinterpret_cast<double*>(arena + lay.off_phi_cur); }
   const float2* rope() const { return reinterpret_cast<const float2*>(arena + lay.off_rope); }
+  // cos/sin table of the place whose first frame has temporal row t_index:
+  // the Ref place (row 0) or block place k at row ref_frames + k block_frames
+  const float2* place_cs(int t_index) const {
+    const float2* base = reinterpret_cast<const float2*>(arena + lay.off_ptab);
+    const size_t np = cfg.head_dim / 2;
+    if (t_index == 0) return base;
+    const int k = (t_index - cfg.ref_frames) / cfg.block_frames;
+    return base + ((size_t)lay.tr + (size_t)k * lay.tb) * np;
+  }
   int bs_static() const { return 0; }
   // Keys of window slot j rotated at window place p (0 = oldest, W-2 = newest)
   // for layer l.
@@ -316,11 +357,21 @@ RopeGeom rope_geom(const pr_sink_cache* c) {
   return g;
 }
 
+// n = i / per_tok for chunk indices i < n_tok * per_tok.
+ChunkDiv chunk_div(const pr_sink_cache* c, int n_tok) {
+  ChunkDiv d{};
+  d.per_tok = (uint32_t)(c->cfg.n_heads * c->cfg.head_dim * c->lay.elem / 16);
+  d.magic = magic_for(d.per_tok);
+  d.exact = magic_exact(d.per_tok, (uint32_t)((uint64_t)n_tok * d.per_tok));
+  d.np = c->cfg.head_dim / 2;
+  return d;
+}
+
 // Rotation launch over n_tok tokens per layer; consecutive layers of source
 // and destination lie layer_bytes apart.
 RotParams rot_params(const pr_sink_cache* c, int n_tok, size_t layer_bytes) {
   RotParams r{};
-  r.g = rope_geom(c);
+  r.cd = chunk_div(c, n_tok);
   r.st = c->state();
   r.block_base = c->block_slot(0);
   r.slot_bytes = (int64_t)c->lay.slot_b;
@@ -332,12 +383,12 @@ RotParams rot_params(const pr_sink_cache* c, int n_tok, size_t layer_bytes) {
   return r;
 }
 
-void add_job(RotParams& r, const void* src, void* dst, int t_index) {
+void add_job(const pr_sink_cache* c, RotParams& r, const void* src, void* dst, int t_index) {
   RotJob& j = r.job[r.n_jobs++];
   j.src = static_cast<const char*>(src);
   j.dst = static_cast<char*>(dst);
   j.dst_off = 0;
-  j.t_index = t_index;
+  j.cs = c->place_cs(t_index);
   j.from_state = 0;
 }
 
@@ -424,6 +475,9 @@ int cache_init(const pr_sink_config* cfg, void* arena_dev, size_t arena_bytes, v
     std::vector<uint32_t> tab = rope_table(cfg, L);
     PRS_HIP(hipMemcpyAsync(a + L.off_rope, tab.data(), tab.size() * sizeof(uint32_t),
                            hipMemcpyHostToDevice, s));
+    std::vector<uint32_t> ptab = place_tables(cfg, L, tab);
+    PRS_HIP(hipMemcpyAsync(a + L.off_ptab, ptab.data(), ptab.size() * sizeof(uint32_t),
+                           hipMemcpyHostToDevice, s));
     PRS_HIP(launch_state_init(reinterpret_cast<DevState*>(a + L.off_state), s));
     PRS_HIP(hipStreamSynchronize(s));
   }
@@ -488,7 +542,7 @@ int pr_sink_set_ref(pr_sink_cache* c, int32_t layer, const void* k_raw, const vo
                             nullptr, nullptr, block_bytes(c, L.tr), s));
     // the Ref Sink's place never moves: rotate its keys once
     RotParams r = rot_params(c, L.tr, L.kv_r);
-    add_job(r, ref + c->k_off(layer, L.kv_r), ref + c->r_off(layer, L.kv_r), 0);
+    add_job(c, r, ref + c->k_off(layer, L.kv_r), ref + c->r_off(layer, L.kv_r), 0);
     PRS_HIP(launch_rope_follow(r, 1, s));
     PRS_HIP(mark(s, c->ref[layer]));
   }
@@ -582,7 +636,7 @@ int prsink::attend_with_workspace(pr_sink_cache* c, int32_t layer, const void* q
   char* cur_rot = ws ? static_cast<char*>(ws->cur_rot) : c->arena + L.off_cur_rot;
   {
     RotParams r = rot_params(c, L.tb, 0);
-    add_job(r, k_cur_raw, cur_rot, t_index[n_seg - 1]);
+    add_job(c, r, k_cur_raw, cur_rot, t_index[n_seg - 1]);
     PRS_HIP(launch_rope_follow(r, 1, st));
   }
   AttnParams p{};
@@ -656,7 +710,7 @@ int pr_sink_clean_kv_write(pr_sink_cache* c, int32_t layer, const void* k_raw, c
     CleanWrite cw{};
     cw.k_src = static_cast<const char*>(k_raw);
     cw.v_src = static_cast<const char*>(v_raw);
-    cw.g = rope_geom(c);
+    cw.cd = chunk_div(c, L.tb);
     cw.n_tok = L.tb;
     cw.n_heads = g.n_heads;
     cw.head_dim = g.head_dim;
@@ -670,7 +724,7 @@ int pr_sink_clean_kv_write(pr_sink_cache* c, int32_t layer, const void* k_raw, c
     for (int p = g.window_slots - 2; p >= 0; --p) {
       CleanDst& d = cw.dst[0];
       d.k_rot[d.n_rot] = c->window_rot(j, p, layer);
-      d.t_index[d.n_rot++] = c->window_t(p);
+      d.cs[d.n_rot++] = c->place_cs(c->window_t(p));
     }
     if (b == 0) {  // block 0 is also the Static Sink, from block 1 on
       char* st = c->block_slot(c->bs_static());
@@ -678,7 +732,7 @@ int pr_sink_clean_kv_write(pr_sink_cache* c, int32_t layer, const void* k_raw, c
       d.k = st + c->k_off(layer, L.kv_b);
       d.v = st + c->v_off(layer, L.kv_b);
       d.k_rot[0] = st + c->r_off(layer, L.kv_b);
-      d.t_index[0] = g.ref_frames;
+      d.cs[0] = c->place_cs(g.ref_frames);
       d.n_rot = 1;
     }
     // the window slot last held block b-W: its last reader was the previous
@@ -736,7 +790,7 @@ int pr_sink_bank_update(pr_sink_cache* c, int32_t block, void* stream) {
       // the Dynamic Sink's place, the only place a bank entry is attended from
       PRS_HIP(launch_slot_copy(c->block_slot(0), L.slot_b, 2 * L.kv_b * g.n_layers, c->state(), s));
       RotParams r = rot_params(c, L.tb, L.kv_b);
-      add_job(r, c->block_slot(ws) + c->k_off(0, L.kv_b), nullptr, g.ref_frames + g.block_frames);
+      add_job(c, r, c->block_slot(ws) + c->k_off(0, L.kv_b), nullptr, g.ref_frames + g.block_frames);
       r.job[0].from_state = 1;
       r.job[0].dst_off = (int64_t)c->r_off(0, L.kv_b);
       PRS_HIP(launch_rope_follow(r, g.n_layers, s));

@@ -100,19 +100,34 @@ struct DevState {
   double best;             // the open block's best dot product with the bank (-inf: empty bank)
 };
 
-// One RoPE-follow job: rotate raw keys [n_tok][H][d] of n_layers layers at the
-// positions of a segment whose first frame has temporal row t_index.
+// cos/sin of one place in the cache (Ref, Static, Dynamic, a window place, the
+// current block): float2 (cos, sin) [token][pair] for every token a block (or
+// the Ref Sink) has at that place and every RoPE pair of a head, in head order
+// (t band pairs, then h, then w).  The places are fixed by the config, so the
+// host fills these tables once, from the same angles as the band table.
+// Chunk c (16 bytes) of a head row at token n needs pairs [4c, 4c+4) (bf16) or
+// [2c, 2c+2) (fp32): one 32- or 16-byte read at cs + n * np + pair.
+
+// One RoPE-follow job: rotate raw keys [n_tok][H][d] of n_layers layers with
+// the cos/sin table of the place they take.
 struct RotJob {
   const char* src;      // raw K of layer 0
   char* dst;            // rotated K of layer 0; ignored when from_state
   int64_t dst_off;      // from_state: byte offset of layer 0's rotated K inside a block slot
-  int32_t t_index;
+  const float2* cs;     // cos/sin table of the place
   int32_t from_state;   // 1: destination slot = device state's copy_dst, skipped when copy_src < 0
+};
+
+// Chunk index -> token: n = i / per_tok by multiply-high when exact (the host
+// checks it over the chunk range), else by division.
+struct ChunkDiv {
+  uint32_t per_tok, magic, exact;
+  int32_t np;           // RoPE pairs per head (head_dim / 2)
 };
 
 struct RotParams {
   RotJob job[kMaxRotJobs];
-  RopeGeom g;
+  ChunkDiv cd;
   const DevState* st;
   char* block_base;     // first block slot (from_state jobs)
   int64_t slot_bytes;   // block slot size (from_state jobs)
@@ -125,20 +140,19 @@ struct RotParams {
 constexpr int kMaxRot = kMaxSegments - 4;
 
 // One destination of a clean write: raw K, V and n_rot copies of K, copy i
-// rotated at the place whose first frame has temporal row t_index[i].
-// k == nullptr: unused.
+// rotated with the cos/sin table cs[i] of its place.  k == nullptr: unused.
 struct CleanDst {
   char* k;
   char* v;
   char* k_rot[kMaxRot];
-  int32_t t_index[kMaxRot];
+  const float2* cs[kMaxRot];
   int32_t n_rot;
 };
 struct CleanWrite {
   const char* k_src;    // clean K of one layer, [n_tok][H][d]
   const char* v_src;
   CleanDst dst[2];      // the window slot; the Static Sink (block 0 only)
-  RopeGeom g;
+  ChunkDiv cd;
   int32_t n_tok, n_heads, head_dim, elem;
 };
 

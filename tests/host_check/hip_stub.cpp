@@ -164,6 +164,8 @@ hipError_t launch_rope_follow(const RotParams& p, int n_layers, hipStream_t s) {
   const size_t n = (size_t)p.n_tok * p.n_heads * p.head_dim * p.elem;
   for (int j = 0; j < p.n_jobs; ++j) {
     const RotJob& jb = p.job[j];
+    inside(jb.cs, (size_t)p.n_tok * p.cd.np * 8, "rope_follow: cos/sin table of the place");
+    if (p.cd.per_tok * 16 != (uint32_t)(p.n_heads * p.head_dim * p.elem)) stub::error("rope_follow: chunks per token");
     for (int l = 0; l < n_layers; ++l) {
       inside(jb.src + (size_t)l * p.layer_bytes, n, "rope_follow: source");
       if (jb.from_state) {
@@ -199,7 +201,10 @@ hipError_t launch_clean_write(const CleanWrite& p, hipStream_t s) {
     if (!d.k) continue;
     inside(d.k, n, "clean_write: raw K destination");
     inside(d.v, n, "clean_write: V destination");
-    for (int r = 0; r < d.n_rot; ++r) inside(d.k_rot[r], n, "clean_write: rotated K destination");
+    for (int r = 0; r < d.n_rot; ++r) {
+      inside(d.k_rot[r], n, "clean_write: rotated K destination");
+      inside(d.cs[r], (size_t)p.n_tok * p.cd.np * 8, "clean_write: cos/sin table of the place");
+    }
   }
   stub::log_launch("clean_write", s);
   return hipSuccess;

@@ -49,6 +49,9 @@ def test_arena_bytes_closed_form():
         kv = 3 * cfg.n_layers * row * (pad(cfg.ref_tokens) + slots * pad(cfg.block_tokens))
         kv += cfg.window_slots * max(0, cfg.window_slots - 2) * cfg.n_layers * row * pad(cfg.block_tokens)
         kv += row * pad(cfg.block_tokens)
+        # cos/sin tables of every place (fp32 pairs): the Ref Sink's, then the
+        # Static, Dynamic, W-1 window and current places of a block
+        kv += 8 * (cfg.head_dim // 2) * (cfg.ref_tokens + (cfg.window_slots + 2) * cfg.block_tokens)
         if cfg.dtype == synth.DTYPE_BF16:
             # split attention jobs: up to 4 pieces of each of up to 32 jobs per
             # XCD (8 XCDs), one fp32 partial record per piece (256 rows x d of
