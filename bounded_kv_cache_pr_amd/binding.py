@@ -244,7 +244,8 @@ class PRSinkCache:
 
     def slot_view(self, slot: int, layer: int, rotated: bool = False):
         """Torch views of one slot's raw K and V, [t_pad][H][d] each; with
-        rotated=True also its rotated K."""
+        rotated=True also its rotated K.  The raw K is None where the cache
+        keeps none (the Static Sink and bank entries)."""
         k, v, r, tp = c_void_p(), c_void_p(), c_void_p(), c_int32()
         check(lib().pr_sink_slot_view(self._h, slot, layer, byref(k), byref(v), byref(r), byref(tp)))
         c = self.cfg
@@ -253,6 +254,8 @@ class PRSinkCache:
         base = self.arena.data_ptr()
 
         def view(ptr):
+            if not ptr:
+                return None
             t = self.arena[ptr - base:ptr - base + n * esz].view(self.torch_dtype)
             return t.view(tp.value, c.n_heads, c.head_dim)
 

@@ -47,17 +47,18 @@ __global__ __launch_bounds__(256) void kv_write_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// slot_copy: grid-stride 16-byte copy of the first copy_bytes of one block
-// slot to another.  Reads the (source, destination) pair from device state; a
-// negative source means there is nothing to copy.
+// slot_copy: grid-stride 16-byte copy of copy_bytes at byte offset copy_off of
+// one block slot to the same place in another.  Reads the (source,
+// destination) pair from device state; a negative source means there is
+// nothing to copy.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void slot_copy_kernel(uint8_t* __restrict__ base,
-                                                        size_t slot_bytes, size_t copy_bytes,
+                                                        size_t slot_bytes, size_t copy_off, size_t copy_bytes,
                                                         const DevState* __restrict__ st) {
   const int src = st->copy_src, dst = st->copy_dst;
   if (src < 0 || src == dst) return;
-  const uint4* __restrict__ s = reinterpret_cast<const uint4*>(base + (size_t)src * slot_bytes);
-  uint4* __restrict__ d = reinterpret_cast<uint4*>(base + (size_t)dst * slot_bytes);
+  const uint4* __restrict__ s = reinterpret_cast<const uint4*>(base + (size_t)src * slot_bytes + copy_off);
+  uint4* __restrict__ d = reinterpret_cast<uint4*>(base + (size_t)dst * slot_bytes + copy_off);
   const size_t n = copy_bytes / 16;
   const size_t stride = (size_t)gridDim.x * blockDim.x;
   size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -152,8 +153,9 @@ __global__ __launch_bounds__(256) void rope_follow_kernel(const RotParams p) {
 // ---------------------------------------------------------------------------
 // clean_write: the clean K/V of one layer of the block being closed go to its
 // window slot, raw, together with its keys rotated at every window place the
-// block takes while it stays in the window (newest first); for block 0 the
-// raw tensors also go to the Static Sink, with the keys rotated at its place.
+// block takes while it stays in the window (newest first); for block 0 the V
+// also goes to the Static Sink, with the keys rotated at its place (a
+// destination without k keeps no raw keys).
 // One pass reads the clean keys once, and no key is rotated again when the
 // window slides.  Thread = one 16-byte chunk of K and of V.
 // ---------------------------------------------------------------------------
@@ -170,8 +172,8 @@ __global__ __launch_bounds__(256) void clean_write_kernel(const CleanWrite p) {
 #pragma unroll
     for (int d = 0; d < 2; ++d) {
       const CleanDst& o = p.dst[d];
-      if (!o.k) continue;
-      st_nt(reinterpret_cast<uint4*>(o.k) + i, k);
+      if (!o.v) continue;
+      if (o.k) st_nt(reinterpret_cast<uint4*>(o.k) + i, k);
       st_nt(reinterpret_cast<uint4*>(o.v) + i, v);
 #pragma unroll
       for (int r = 0; r < kMaxRot; ++r) {
@@ -452,13 +454,13 @@ hipError_t launch_clean_write(const CleanWrite& p, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_slot_copy(char* block_base, size_t slot_bytes, size_t copy_bytes,
+hipError_t launch_slot_copy(char* block_base, size_t slot_bytes, size_t copy_off, size_t copy_bytes,
                             const DevState* st, hipStream_t s) {
   const size_t n16 = copy_bytes / 16;
   size_t blocks = (n16 + 255) / 256;
   if (blocks > 256 * 16) blocks = 256 * 16;
   hipLaunchKernelGGL(slot_copy_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
-                     reinterpret_cast<uint8_t*>(block_base), slot_bytes, copy_bytes, st);
+                     reinterpret_cast<uint8_t*>(block_base), slot_bytes, copy_off, copy_bytes, st);
   return hipGetLastError();
 }
 

@@ -729,7 +729,7 @@ int pr_sink_clean_kv_write(pr_sink_cache* c, int32_t layer, const void* k_raw, c
     if (b == 0) {  // block 0 is also the Static Sink, from block 1 on
       char* st = c->block_slot(c->bs_static());
       CleanDst& d = cw.dst[1];
-      d.k = st + c->k_off(layer, L.kv_b);
+      d.k = nullptr;  // the Static Sink is attended rotated only: no raw keys
       d.v = st + c->v_off(layer, L.kv_b);
       d.k_rot[0] = st + c->r_off(layer, L.kv_b);
       d.cs[0] = c->place_cs(g.ref_frames);
@@ -786,9 +786,10 @@ int pr_sink_bank_update(pr_sink_cache* c, int32_t block, void* stream) {
       // the next retrieval needs the decision only (see pr_sink_retrieve)
       PRS_HIP(mark(s, c->dec));
       PRS_HIP(after_clean());
-      // the written entry gets the block's raw K and V, and its K rotated at
-      // the Dynamic Sink's place, the only place a bank entry is attended from
-      PRS_HIP(launch_slot_copy(c->block_slot(0), L.slot_b, 2 * L.kv_b * g.n_layers, c->state(), s));
+      // the written entry gets the block's V, and its K rotated at the
+      // Dynamic Sink's place, the only place a bank entry is attended from
+      // (rotated from the window slot's raw keys; an entry keeps no raw keys)
+      PRS_HIP(launch_slot_copy(c->block_slot(0), L.slot_b, c->v_off(0, L.kv_b), L.kv_b * g.n_layers, c->state(), s));
       RotParams r = rot_params(c, L.tb, L.kv_b);
       add_job(c, r, c->block_slot(ws) + c->k_off(0, L.kv_b), nullptr, g.ref_frames + g.block_frames);
       r.job[0].from_state = 1;
@@ -852,7 +853,9 @@ int pr_sink_slot_view(const pr_sink_cache* c, int32_t slot, int32_t layer, void*
     kv = L.kv_b;
     *t_pad_out = L.tb_pad;
   }
-  *k_dev = base + c->k_off(layer, kv);
+  // raw keys are kept for the Ref Sink and the window slots only
+  const bool raw = slot == PR_SINK_SLOT_REF || (slot >= PR_SINK_SLOT_WINDOW0 && slot < PR_SINK_SLOT_WINDOW0 + c->cfg.window_slots);
+  *k_dev = raw ? base + c->k_off(layer, kv) : nullptr;
   *v_dev = base + c->v_off(layer, kv);
   if (k_rot_dev) *k_rot_dev = base + c->r_off(layer, kv);
   const int W = c->cfg.window_slots;

@@ -139,8 +139,9 @@ struct RotParams {
 // window (at most kMaxSegments - 4 of them).
 constexpr int kMaxRot = kMaxSegments - 4;
 
-// One destination of a clean write: raw K, V and n_rot copies of K, copy i
-// rotated with the cos/sin table cs[i] of its place.  k == nullptr: unused.
+// One destination of a clean write: raw K (k == nullptr: not kept), V and
+// n_rot copies of K, copy i rotated with the cos/sin table cs[i] of its place.
+// v == nullptr: unused.
 struct CleanDst {
   char* k;
   char* v;
@@ -163,7 +164,7 @@ hipError_t launch_rope_follow(const RotParams& p, int n_layers, hipStream_t s);
 hipError_t launch_kv_write(const void* k_src, const void* v_src, void* k_dst0, void* v_dst0,
                            void* k_dst1, void* v_dst1, size_t bytes, hipStream_t s);
 hipError_t launch_clean_write(const CleanWrite& p, hipStream_t s);
-hipError_t launch_slot_copy(char* block_base, size_t slot_bytes, size_t copy_bytes,
+hipError_t launch_slot_copy(char* block_base, size_t slot_bytes, size_t copy_off, size_t copy_bytes,
                             const DevState* st, hipStream_t s);
 // Bank update rules of one cache (pr_sink_config's bank fields).
 struct BankRule {

@@ -242,7 +242,9 @@ int pr_sink_bank_state(pr_sink_cache* c, int32_t* ids_host, double* fp_host,
 /* Device pointers to the raw K, the V and the rotated K of one slot and
  * layer, for inspection.  All are [t_pad][H][d], token-major like the tensors
  * passed in; t_pad (a multiple of 64; the padding rows are zero) goes to
- * *t_pad_out.  The rotated K holds the keys rotated at the place the slot's
+ * *t_pad_out.  Raw keys are kept for the Ref Sink and the window slots only
+ * (the Static Sink and bank entries are attended rotated, and rotated from
+ * the window slot's raw keys when written): *k_dev receives NULL for them.  The rotated K holds the keys rotated at the place the slot's
  * block takes in the window of the open block (of the next one between
  * blocks); for the block written in it, or one that has left the window, the
  * newest window place.  Static: at the Static Sink's place; a bank entry: at

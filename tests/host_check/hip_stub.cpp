@@ -198,8 +198,8 @@ hipError_t launch_clean_write(const CleanWrite& p, hipStream_t s) {
   inside(p.k_src, n, "clean_write: k");
   inside(p.v_src, n, "clean_write: v");
   for (const CleanDst& d : p.dst) {
-    if (!d.k) continue;
-    inside(d.k, n, "clean_write: raw K destination");
+    if (!d.v) continue;
+    if (d.k) inside(d.k, n, "clean_write: raw K destination");
     inside(d.v, n, "clean_write: V destination");
     for (int r = 0; r < d.n_rot; ++r) {
       inside(d.k_rot[r], n, "clean_write: rotated K destination");
@@ -210,8 +210,11 @@ hipError_t launch_clean_write(const CleanWrite& p, hipStream_t s) {
   return hipSuccess;
 }
 
-hipError_t launch_slot_copy(char* base, size_t slot_bytes, size_t copy_bytes, const DevState* st, hipStream_t s) {
-  for (int d = 0; d < stub::block_slots_hint; ++d) inside(base + (size_t)d * slot_bytes, copy_bytes, "slot_copy");
+hipError_t launch_slot_copy(char* base, size_t slot_bytes, size_t copy_off, size_t copy_bytes, const DevState* st,
+                            hipStream_t s) {
+  if (copy_off + copy_bytes > slot_bytes) stub::error("slot_copy: range past the slot");
+  for (int d = 0; d < stub::block_slots_hint; ++d)
+    inside(base + (size_t)d * slot_bytes + copy_off, copy_bytes, "slot_copy");
   inside(st, sizeof *st, "slot_copy: state");
   stub::log_launch("slot_copy", s);
   return hipSuccess;

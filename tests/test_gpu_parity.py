@@ -161,12 +161,18 @@ class Stream:
             assert not got[T:].any()
 
     def check_slot_bytes(self, slot, block, layer):
-        """Stored raw K/V of a slot equal the block's clean K/V bit for bit; padding is zero."""
+        """Stored V of a slot (and, in a window slot, its raw K) equal the block's
+        clean K/V bit for bit; padding is zero.  The Static Sink and bank entries
+        keep no raw keys (their rotated keys are checked by check_rotations)."""
         kt, vt = self.cache.slot_view(slot, layer)
         k, v = self.clean(block, layer)
         T = self.cfg.block_tokens
+        W = self.cfg.window_slots
+        is_window = binding.SLOT_WINDOW0 <= slot < binding.SLOT_WINDOW0 + W
+        assert (kt is not None) == is_window, f"slot {slot}: raw keys kept only in window slots"
         bits = torch.int16 if self.dt == torch.bfloat16 else torch.int32
-        for got, src in ((kt.cpu(), k), (vt.cpu(), v)):
+        pairs = ((kt.cpu(), k), (vt.cpu(), v)) if is_window else ((vt.cpu(), v),)
+        for got, src in pairs:
             want = torch.from_numpy(np.ascontiguousarray(src)).to(self.dt)
             assert torch.equal(got[:T].contiguous().view(bits), want.view(bits))
             assert not got[T:].any()
