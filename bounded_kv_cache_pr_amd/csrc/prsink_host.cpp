@@ -75,7 +75,7 @@ struct Layout {
   size_t kv_b, slot_b;   // block slot: one tensor of one layer, whole slot
   size_t kv_r, slot_r;   // Ref slot
   size_t off_state, off_phi_bank, off_phi_cur, off_rope, off_ptab, off_cur_rot, off_part, off_cnt, off_ref,
-      off_blocks, off_wrot, total;
+      off_blocks, off_wraw, off_wrot, total;
   size_t wrot_b;             // per window slot: its keys rotated at the older window places
   size_t n_part_rec, n_cnt;  // partial records and counters of split attention jobs
   int n_t, np_t, np_h, np_w, rope_h_off, rope_w_off, rope_entries;
@@ -131,7 +131,9 @@ Layout make_layout(const pr_sink_config* c) {
   L.tr_pad = pad_tokens(L.tr);
   const size_t hd = (size_t)c->n_heads * c->head_dim * L.elem;
   L.kv_b = align_up(hd * L.tb_pad, 256);
-  L.slot_b = align_up(3 * L.kv_b * c->n_layers, kAlign);
+  // a block slot holds V and the keys rotated at the slot's place; the raw
+  // keys of the window's blocks live in a ring-indexed area of their own
+  L.slot_b = align_up(2 * L.kv_b * c->n_layers, kAlign);
   L.kv_r = align_up(hd * L.tr_pad, 256);
   L.slot_r = align_up(3 * L.kv_r * c->n_layers, kAlign);
   // Static, the window, the bank; the Dynamic Sink is a reference to a bank
@@ -174,6 +176,8 @@ Layout make_layout(const pr_sink_config* c) {
   off += L.slot_r;
   L.off_blocks = off;
   off += L.slot_b * L.n_block_slots;
+  L.off_wraw = off;  // raw keys of window slot j: W x n_layers tensors
+  off += align_up((size_t)c->window_slots * c->n_layers * L.kv_b, kAlign);
   // a window block is attended at W-1 places; the block slot holds its keys
   // rotated at the newest one, this area the W-2 older ones
   L.off_wrot = off;
@@ -276,9 +280,17 @@ struct pr_sink_cache {
   char* block_slot(int bs) const { return arena + lay.off_blocks + (size_t)bs * lay.slot_b; }
   char* ref_slot() const { return arena + lay.off_ref; }
   // raw K, V and rotated K of one layer inside a slot whose tensors are kv bytes
-  size_t k_off(int l, size_t kv) const { return (size_t)l * kv; }
-  size_t v_off(int l, size_t kv) const { return ((size_t)cfg.n_layers + l) * kv; }
-  size_t r_off(int l, size_t kv) const { return (2 * (size_t)cfg.n_layers + l) * kv; }
+  // Ref slot: raw K, V and rotated K of layer l
+  size_t ref_k(int l) const { return (size_t)l * lay.kv_r; }
+  size_t ref_v(int l) const { return ((size_t)cfg.n_layers + l) * lay.kv_r; }
+  size_t ref_r(int l) const { return (2 * (size_t)cfg.n_layers + l) * lay.kv_r; }
+  // block slot: V and rotated K of layer l
+  size_t blk_v(int l) const { return (size_t)l * lay.kv_b; }
+  size_t blk_r(int l) const { return ((size_t)cfg.n_layers + l) * lay.kv_b; }
+  // raw keys of the block in window slot j, layer l
+  char* window_raw(int j, int l) const {
+    return arena + lay.off_wraw + ((size_t)j * cfg.n_layers + l) * lay.kv_b;
+  }
   DevState* state() const { return reinterpret_cast<DevState*>(arena + lay.off_state); }
   double* phi_bank() const { return reinterpret_cast<double*>(arena + lay.off_phi_bank); }
   double* phi_cur() const { return reinterpret_cast<double*>(arena + lay.off_phi_cur); }
@@ -296,7 +308,7 @@ struct pr_sink_cache {
   // Keys of window slot j rotated at window place p (0 = oldest, W-2 = newest)
   // for layer l.
   char* window_rot(int j, int p, int l) const {
-    if (p == cfg.window_slots - 2) return block_slot(bs_window(j)) + r_off(l, lay.kv_b);
+    if (p == cfg.window_slots - 2) return block_slot(bs_window(j)) + blk_r(l);
     return arena + lay.off_wrot + (size_t)j * lay.wrot_b + ((size_t)p * cfg.n_layers + l) * lay.kv_b;
   }
   // First temporal row of window place p.
@@ -538,11 +550,11 @@ int pr_sink_set_ref(pr_sink_cache* c, int32_t layer, const void* k_raw, const vo
     // layer, possibly on another stream, must land first (write after write)
     PRS_HIP(after(s, c->attn));
     PRS_HIP(after(s, c->ref[layer]));
-    PRS_HIP(launch_kv_write(k_raw, v_raw, ref + c->k_off(layer, L.kv_r), ref + c->v_off(layer, L.kv_r),
+    PRS_HIP(launch_kv_write(k_raw, v_raw, ref + c->ref_k(layer), ref + c->ref_v(layer),
                             nullptr, nullptr, block_bytes(c, L.tr), s));
     // the Ref Sink's place never moves: rotate its keys once
     RotParams r = rot_params(c, L.tr, L.kv_r);
-    add_job(c, r, ref + c->k_off(layer, L.kv_r), ref + c->r_off(layer, L.kv_r), 0);
+    add_job(c, r, ref + c->ref_k(layer), ref + c->ref_r(layer), 0);
     PRS_HIP(launch_rope_follow(r, 1, s));
     PRS_HIP(mark(s, c->ref[layer]));
   }
@@ -650,8 +662,8 @@ int prsink::attend_with_workspace(pr_sink_cache* c, int32_t layer, const void* q
     sg.tok = (int64_t)g.n_heads * D;
     sg.head = D;
     if (s == 0) {
-      sg.k = c->ref_slot() + c->r_off(layer, L.kv_r);
-      sg.v = c->ref_slot() + c->v_off(layer, L.kv_r);
+      sg.k = c->ref_slot() + c->ref_r(layer);
+      sg.v = c->ref_slot() + c->ref_v(layer);
     } else if (s == n_seg - 1) {  // current block: rotated copy, caller's V
       sg.k = cur_rot;
       sg.v = v_cur_raw;
@@ -660,18 +672,18 @@ int prsink::attend_with_workspace(pr_sink_cache* c, int32_t layer, const void* q
       if (tokens[s] > 0) {
         p.dyn_seg = s;
         p.dyn_r = &c->state()->last_r;
-        p.dyn_k0 = c->block_slot(c->bs_bank(0)) + c->r_off(layer, L.kv_b);
-        p.dyn_v0 = c->block_slot(c->bs_bank(0)) + c->v_off(layer, L.kv_b);
+        p.dyn_k0 = c->block_slot(c->bs_bank(0)) + c->blk_r(layer);
+        p.dyn_v0 = c->block_slot(c->bs_bank(0)) + c->blk_v(layer);
         p.dyn_stride = (int64_t)L.slot_b;
       }
     } else if (s == 1) {  // Static Sink
-      sg.k = c->block_slot(c->bs_static()) + c->r_off(layer, L.kv_b);
-      sg.v = c->block_slot(c->bs_static()) + c->v_off(layer, L.kv_b);
+      sg.k = c->block_slot(c->bs_static()) + c->blk_r(layer);
+      sg.v = c->block_slot(c->bs_static()) + c->blk_v(layer);
     } else {  // window place s - 3: block b - (W-1) + (s-3)
       const int id = b - (g.window_slots - 1) + (s - 3);
       const int j = id >= 0 ? id % g.window_slots : 0;
       sg.k = c->window_rot(j, s - 3, layer);
-      sg.v = c->block_slot(c->bs_window(j)) + c->v_off(layer, L.kv_b);
+      sg.v = c->block_slot(c->bs_window(j)) + c->blk_v(layer);
     }
   }
   p.q = q_raw;
@@ -719,8 +731,8 @@ int pr_sink_clean_kv_write(pr_sink_cache* c, int32_t layer, const void* k_raw, c
     // takes from the next block on, newest first (none when the window holds
     // only the current block)
     const int j = b % g.window_slots;
-    cw.dst[0].k = w + c->k_off(layer, L.kv_b);
-    cw.dst[0].v = w + c->v_off(layer, L.kv_b);
+    cw.dst[0].k = c->window_raw(b % g.window_slots, layer);
+    cw.dst[0].v = w + c->blk_v(layer);
     for (int p = g.window_slots - 2; p >= 0; --p) {
       CleanDst& d = cw.dst[0];
       d.k_rot[d.n_rot] = c->window_rot(j, p, layer);
@@ -730,8 +742,8 @@ int pr_sink_clean_kv_write(pr_sink_cache* c, int32_t layer, const void* k_raw, c
       char* st = c->block_slot(c->bs_static());
       CleanDst& d = cw.dst[1];
       d.k = nullptr;  // the Static Sink is attended rotated only: no raw keys
-      d.v = st + c->v_off(layer, L.kv_b);
-      d.k_rot[0] = st + c->r_off(layer, L.kv_b);
+      d.v = st + c->blk_v(layer);
+      d.k_rot[0] = st + c->blk_r(layer);
       d.cs[0] = c->place_cs(g.ref_frames);
       d.n_rot = 1;
     }
@@ -789,11 +801,11 @@ int pr_sink_bank_update(pr_sink_cache* c, int32_t block, void* stream) {
       // the written entry gets the block's V, and its K rotated at the
       // Dynamic Sink's place, the only place a bank entry is attended from
       // (rotated from the window slot's raw keys; an entry keeps no raw keys)
-      PRS_HIP(launch_slot_copy(c->block_slot(0), L.slot_b, c->v_off(0, L.kv_b), L.kv_b * g.n_layers, c->state(), s));
+      PRS_HIP(launch_slot_copy(c->block_slot(0), L.slot_b, c->blk_v(0), L.kv_b * g.n_layers, c->state(), s));
       RotParams r = rot_params(c, L.tb, L.kv_b);
-      add_job(c, r, c->block_slot(ws) + c->k_off(0, L.kv_b), nullptr, g.ref_frames + g.block_frames);
+      add_job(c, r, c->window_raw(block % g.window_slots, 0), nullptr, g.ref_frames + g.block_frames);
       r.job[0].from_state = 1;
-      r.job[0].dst_off = (int64_t)c->r_off(0, L.kv_b);
+      r.job[0].dst_off = (int64_t)c->blk_r(0);
       PRS_HIP(launch_rope_follow(r, g.n_layers, s));
       PRS_HIP(mark(s, c->bank));
     }
@@ -842,22 +854,21 @@ int pr_sink_slot_view(const pr_sink_cache* c, int32_t slot, int32_t layer, void*
   if (slot < 0 || slot >= n_slots) return fail(PR_SINK_EINVAL, "slot %d out of range", slot);
   if (slot == PR_SINK_SLOT_DYNAMIC)
     return fail(PR_SINK_EINVAL, "the Dynamic Sink is bank entry r (pr_sink_retrieve's slot_out), not a slot of its own; view that bank entry");
-  char* base;
-  size_t kv;
   if (slot == PR_SINK_SLOT_REF) {
-    base = c->ref_slot();
-    kv = L.kv_r;
+    char* base = c->ref_slot();
     *t_pad_out = L.tr_pad;
-  } else {
-    base = c->block_slot(slot == PR_SINK_SLOT_STATIC ? c->bs_static() : slot - PR_SINK_SLOT_WINDOW0 + 1);
-    kv = L.kv_b;
-    *t_pad_out = L.tb_pad;
+    *k_dev = base + c->ref_k(layer);
+    *v_dev = base + c->ref_v(layer);
+    if (k_rot_dev) *k_rot_dev = base + c->ref_r(layer);
+    return PR_SINK_OK;
   }
-  // raw keys are kept for the Ref Sink and the window slots only
-  const bool raw = slot == PR_SINK_SLOT_REF || (slot >= PR_SINK_SLOT_WINDOW0 && slot < PR_SINK_SLOT_WINDOW0 + c->cfg.window_slots);
-  *k_dev = raw ? base + c->k_off(layer, kv) : nullptr;
-  *v_dev = base + c->v_off(layer, kv);
-  if (k_rot_dev) *k_rot_dev = base + c->r_off(layer, kv);
+  // raw keys are kept for the window slots only
+  const bool window = slot >= PR_SINK_SLOT_WINDOW0 && slot < PR_SINK_SLOT_WINDOW0 + c->cfg.window_slots;
+  char* base = c->block_slot(slot == PR_SINK_SLOT_STATIC ? c->bs_static() : slot - PR_SINK_SLOT_WINDOW0 + 1);
+  *t_pad_out = L.tb_pad;
+  *k_dev = window ? c->window_raw(slot - PR_SINK_SLOT_WINDOW0, layer) : nullptr;
+  *v_dev = base + c->blk_v(layer);
+  if (k_rot_dev) *k_rot_dev = base + c->blk_r(layer);
   const int W = c->cfg.window_slots;
   if (k_rot_dev && W >= 2 && slot >= PR_SINK_SLOT_WINDOW0 && slot < PR_SINK_SLOT_WINDOW0 + W) {
     // the copy at the place the slot's block holds in the window of the open

@@ -43,10 +43,12 @@ def test_arena_bytes_closed_form():
         pad = lambda n: -(-n // 64) * 64
         slots = 1 + cfg.window_slots + cfg.bank_size  # Static, window, bank (Dynamic reads a bank entry)
         row = cfg.n_heads * cfg.head_dim * esz
-        # every slot holds raw K, V and rotated K per layer; a window block is
-        # attended at W-1 places, so each window slot keeps W-2 more rotated
-        # copies; plus the current block's rotated K
-        kv = 3 * cfg.n_layers * row * (pad(cfg.ref_tokens) + slots * pad(cfg.block_tokens))
+        # the Ref slot holds raw K, V and rotated K per layer; a block slot V
+        # and rotated K; raw keys are kept for the W window blocks only; a
+        # window block is attended at W-1 places, so each window slot keeps
+        # W-2 more rotated copies; plus the current block's rotated K
+        kv = 3 * cfg.n_layers * row * pad(cfg.ref_tokens) + 2 * cfg.n_layers * row * slots * pad(cfg.block_tokens)
+        kv += cfg.window_slots * cfg.n_layers * row * pad(cfg.block_tokens)
         kv += cfg.window_slots * max(0, cfg.window_slots - 2) * cfg.n_layers * row * pad(cfg.block_tokens)
         kv += row * pad(cfg.block_tokens)
         # cos/sin tables of every place (fp32 pairs): the Ref Sink's, then the
