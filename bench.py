@@ -14,6 +14,10 @@ reuse cached keys.
 --workload 384x672 runs the same step on the 384x672 bucket (Q=3024,
 K=16128) instead.
 
+--attends-per-layer 4 adds the clean forward's own attention call to every
+layer (160 calls per block at 40 layers) as a variant; 3, the denoise steps
+alone, is the headline step.
+
 Prints one JSON line.  `value` is attention TFLOP/s over the whole step (120
 attention calls' algorithmic FLOPs / block time).  The timed blocks carry no
 timing markers.  After them, untimed blocks of the same stream measure the
@@ -44,24 +48,20 @@ POOL = 7                    # distinct input sets per pool (coprime to the layer
 KERNEL_BLOCKS = 2           # untimed blocks whose attention kernels carry HIP events
 
 
-ATTN_SOURCE = os.path.join(ROOT, "bounded_kv_cache_pr_amd", "csrc", "kernels_attn.hip")
-
-
 def counter_record(workload):
     """The committed rocprofv3 counter record of the workload (HBM bytes per attention
-    launch from FETCH_SIZE / WRITE_SIZE; the shader clock and MFMA utilisation where
-    measured), or None when there is none or the kernel source has changed since it was
-    taken."""
-    import hashlib
+    launch from FETCH_SIZE / WRITE_SIZE, cross-checked by the DRAM request counters; the
+    shader clock and MFMA utilisation), or None when there is none or the attention
+    kernel's sources have changed since it was taken."""
+    from bounded_kv_cache_pr_amd.profile_summary import attn_source_sha256
     record = os.path.join(ROOT, "profiles", f"attn_bf16_kernel_{workload}_traffic.json")
     try:
         with open(record) as f:
             rec = json.load(f)
-        with open(ATTN_SOURCE, "rb") as f:
-            sha = hashlib.sha256(f.read()).hexdigest()
+        sha = attn_source_sha256()
     except OSError:
         return None
-    return rec if rec.get("kernels_attn_hip_sha256") == sha else None
+    return rec if rec.get("attn_sources_sha256") == sha else None
 
 
 def attn_flops(cfg) -> float:
@@ -105,6 +105,9 @@ def main():
     ap.add_argument("--streams", type=int, choices=(1, 2), default=2,
                     help="2: clean-KV writes and the bank update on a second stream")
     ap.add_argument("--workload", choices=WORKLOADS, default="480x480")
+    ap.add_argument("--attends-per-layer", type=int, choices=(3, 4), default=3,
+                    help="attention calls per layer and block: the 3 denoise steps, or 4 when the "
+                         "clean forward's own attention is counted too (160 calls at 40 layers)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: the PR-Sink path here runs on a single MI355X "
@@ -121,7 +124,7 @@ def main():
     dev = torch.device("cuda:0")
     base = synth.C3_STREAM_480 if args.workload == "480x480" else synth.C2_384x672
     cfg = base.replace(n_layers=args.layers)
-    L, steps = cfg.n_layers, synth.DENOISE_STEPS
+    L, steps = cfg.n_layers, args.attends_per_layer
     n_blocks = args.warmup + args.steps
     seed = args.seed
 
@@ -209,11 +212,12 @@ def main():
             "workload": f"PR-Sink streamed block at {args.workload}: H={cfg.n_heads}, "
                         f"d={cfg.head_dim}, Q={T}, K={Kc} "
                         f"(Ref {cfg.ref_tokens} + Static/Dynamic/2 window/current {T} each), {L} layers x "
-                        f"{steps} denoise-step attention calls + {L} clean-KV writes + "
+                        f"{steps} attention calls ({'denoise steps' if steps == synth.DENOISE_STEPS else 'denoise steps + the clean forward'}) + {L} clean-KV writes + "
                         "retrieval + bank update",
             "blocks_timed": f"{args.warmup}..{n_blocks - 1}",
             "streams": args.streams,
             "layers": L,
+            "attends_per_layer": steps,
         },
         "attn_ms_per_call": round(attn_avg_ms, 5),
         "attn_kernel_ms": round(kern_avg_ms, 5),

@@ -11,6 +11,7 @@
 // per-block latency independent of stream length).
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -258,10 +259,15 @@ struct pr_sink_cache {
     hipEvent_t ev = nullptr;
     hipStream_t st = nullptr;
     bool set = false;
+    bool pending = false;         // marked but not recorded yet (see defer)
     bool waited = false;          // `seen` already waits for this recording
     hipStream_t seen = nullptr;   // (the null stream is a stream too)
   };
   std::vector<Mark> clean;  // per layer: the last clean write of that layer
+  Mark clean_all;           // every clean write of block clean_all_block (all on one stream)
+  int clean_all_block = -1;
+  hipStream_t clean_stream = nullptr;  // the stream of this block's clean writes so far
+  bool clean_one_stream = true;
   std::vector<Mark> ref;    // per layer: the last Ref Sink write of that layer
   Mark attn;                // the last attention call
   Mark retr;                // the last retrieval
@@ -274,7 +280,7 @@ struct pr_sink_cache {
     auto drop = [](Mark& m) { if (m.ev) (void)hipEventDestroy(m.ev); };
     for (Mark& m : clean) drop(m);
     for (Mark& m : ref) drop(m);
-    drop(attn); drop(retr); drop(dec); drop(bank); drop(done[0]); drop(done[1]);
+    drop(clean_all); drop(attn); drop(retr); drop(dec); drop(bank); drop(done[0]); drop(done[1]);
   }
 
   char* block_slot(int bs) const { return arena + lay.off_blocks + (size_t)bs * lay.slot_b; }
@@ -417,7 +423,15 @@ size_t block_bytes(const pr_sink_cache* c, int n_tok) {
 // costs microseconds between kernels; the three denoise steps of a layer
 // would otherwise each wait for the same clean write).
 hipError_t after(hipStream_t s, pr_sink_cache::Mark& m) {
-  if (!m.set || m.st == s || (m.waited && m.seen == s)) return hipSuccess;
+  if (!m.set || m.st == s) return hipSuccess;
+  if (m.pending) {
+    // recorded now: the event then also covers work queued on m.st since the
+    // mark, which only makes the wait longer, never too short
+    if (hipError_t e = hipEventRecord(m.ev, m.st)) return e;
+    m.pending = false;
+    m.waited = false;
+  }
+  if (m.waited && m.seen == s) return hipSuccess;
   const hipError_t e = hipStreamWaitEvent(s, m.ev, 0);
   if (e == hipSuccess) {
     m.waited = true;
@@ -429,8 +443,21 @@ hipError_t after(hipStream_t s, pr_sink_cache::Mark& m) {
 hipError_t mark(hipStream_t s, pr_sink_cache::Mark& m) {
   m.st = s;
   m.set = true;
+  m.pending = false;
   m.waited = false;
   return hipEventRecord(m.ev, s);
+}
+// mark() without the event record, which after() makes the first time a
+// consumer on another stream waits.  For the attention calls: a record costs
+// the queue a few microseconds between kernels, and their consumers (clean
+// writes, bank updates, Ref writes) come after a whole block of them.  Work
+// that other streams must see at a finer grain (the per-layer clean writes
+// the next block's attention waits for) keeps mark().
+void defer(hipStream_t s, pr_sink_cache::Mark& m) {
+  m.st = s;
+  m.set = true;
+  m.pending = true;
+  m.waited = false;
 }
 
 }  // namespace
@@ -516,7 +543,7 @@ int cache_init(const pr_sink_config* cfg, void* arena_dev, size_t arena_bytes, v
     hipError_t e = hipSuccess;
     for (auto& m : c->clean) if (e == hipSuccess) e = make(m);
     for (auto& m : c->ref) if (e == hipSuccess) e = make(m);
-    for (auto* m : {&c->attn, &c->retr, &c->dec, &c->bank, &c->done[0], &c->done[1]})
+    for (auto* m : {&c->clean_all, &c->attn, &c->retr, &c->dec, &c->bank, &c->done[0], &c->done[1]})
       if (e == hipSuccess) e = make(*m);
     if (e != hipSuccess) {
       delete c;
@@ -637,10 +664,11 @@ int prsink::attend_with_workspace(pr_sink_cache* c, int32_t layer, const void* q
   segment_table(c, tokens, t_index);
   const int n_seg = g.window_slots + 3;
   hipStream_t st = as_stream(stream);
-  // this layer's newest window block (the previous block's clean write), the
-  // retrieval, this layer's Ref Sink, and the previous call (attention calls
-  // share the rotated-current-key scratch and the split-job records)
-  PRS_HIP(after(st, c->clean[layer]));
+  // this layer's newest window block (the previous block's clean write; one
+  // wait covers all layers when they went to one stream), the retrieval, this
+  // layer's Ref Sink, and the previous call (attention calls share the
+  // rotated-current-key scratch and the split-job records)
+  PRS_HIP(after(st, c->clean_all_block == c->next_block - 1 ? c->clean_all : c->clean[layer]));
   PRS_HIP(after(st, c->retr));
   PRS_HIP(after(st, c->ref[layer]));
   PRS_HIP(after(st, c->attn));
@@ -701,7 +729,7 @@ int prsink::attend_with_workspace(pr_sink_cache* c, int32_t layer, const void* q
   if (c->time_start) PRS_HIP(hipEventRecord(c->time_start, st));
   PRS_HIP(launch_attention(p, g.dtype, g.head_dim, c->n_cu, st));
   if (c->time_stop) PRS_HIP(hipEventRecord(c->time_stop, st));
-  PRS_HIP(mark(st, c->attn));
+  defer(st, c->attn);
   return PR_SINK_OK;
 }
 
@@ -758,6 +786,19 @@ int pr_sink_clean_kv_write(pr_sink_cache* c, int32_t layer, const void* k_raw, c
     PRS_HIP(after(s, c->bank));
     PRS_HIP(launch_clean_write(cw, s));
     PRS_HIP(mark(s, c->clean[layer]));
+    const int n_written = (int)std::count(c->written.begin(), c->written.end(), (uint8_t)1);
+    if (n_written == 0) {
+      c->clean_stream = s;
+      c->clean_one_stream = true;
+    } else if (s != c->clean_stream) {
+      c->clean_one_stream = false;
+    }
+    if (n_written + 1 == g.n_layers && c->clean_one_stream) {
+      // the block's last clean write, and all of them on s: the next block's
+      // attention waits once for them all
+      PRS_HIP(mark(s, c->clean_all));
+      c->clean_all_block = b;
+    }
   }
   c->written[layer] = 1;
   return PR_SINK_OK;

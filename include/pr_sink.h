@@ -57,6 +57,10 @@
  * copy of the entry it writes (that entry holds block b, which the retrieval
  * excludes), so the copy overlaps block b+1's attention.  The calls
  * themselves must come from one host thread, in the block order below.
+ * The completion of pr_sink_attend is recorded on its stream only when a
+ * call on another stream first has to wait for it, so a stream passed to
+ * pr_sink_attend must stay alive until the next block's pr_sink_retrieve
+ * returns.
  *
  * Call order per block b = 0, 1, 2, ...:
  *   pr_sink_retrieve(b)  ->  pr_sink_attend(layer) any number of times

@@ -187,7 +187,11 @@ struct Rig {
   }
 };
 
-void stream_checks(int dtype, int window, int bank) {
+// mixed: attention calls alternate between the two streams, and in odd
+// blocks the clean write of layer 0 goes to the attention stream, so the
+// marks recorded on first use and the one-wait-per-block path for clean
+// writes on one stream are crossed with their fallbacks.
+void stream_checks(int dtype, int window, int bank, bool mixed) {
   stub::reset_log();
   Rig g(small_config(dtype, window, bank));
   const pr_sink_config& c = g.c;
@@ -213,10 +217,14 @@ void stream_checks(int dtype, int window, int bank) {
     for (int s = 0; s < 3; ++s)
       for (int l = 0; l < c.n_layers; ++l)
         attn[b].push_back(logged([&] {
-          CHECK(pr_sink_attend(g.h, l, g.q, g.kc, g.vc, g.out, A) == PR_SINK_OK, "attend: %s", pr_sink_last_error());
+          void* const st = mixed && (s * c.n_layers + l) % 2 ? B : A;
+          CHECK(pr_sink_attend(g.h, l, g.q, g.kc, g.vc, g.out, st) == PR_SINK_OK, "attend: %s", pr_sink_last_error());
         }));
     for (int l = 0; l < c.n_layers; ++l)
-      clean[b].push_back(logged([&] { CHECK(pr_sink_clean_kv_write(g.h, l, g.kc, g.vc, B) == PR_SINK_OK, "clean"); }));
+      clean[b].push_back(logged([&] {
+        void* const st = mixed && b % 2 && l == 0 ? A : B;
+        CHECK(pr_sink_clean_kv_write(g.h, l, g.kc, g.vc, st) == PR_SINK_OK, "clean");
+      }));
     upd[b] = logged([&] { CHECK(pr_sink_bank_update(g.h, b, B) == PR_SINK_OK, "bank_update %d", b); });
   }
   for (int b = 0; b < n_blocks; ++b) {
@@ -225,13 +233,19 @@ void stream_checks(int dtype, int window, int bank) {
       if (b == 0) CHECK(ordered(ref[l], attn[b][i]), "attention of layer %d after its Ref Sink", l);
       CHECK(ordered(retr[b], attn[b][i]), "attention after the block's retrieval");
       if (b > 0) CHECK(ordered(clean[b - 1][l], attn[b][i]), "block %d attention of layer %d after the clean write", b, l);
+      // attention calls share the rotated-current-key scratch and split records
+      if (i > 0) CHECK(ordered(attn[b][i - 1], attn[b][i]), "block %d attention call %d after the previous one", b, i);
+      if (i == 0 && b > 0) CHECK(ordered(attn[b - 1].back(), attn[b][i]), "block %d first attention after the last", b);
     }
     for (int l = 0; l < c.n_layers; ++l) {
       CHECK(ordered(retr[b], clean[b][l]), "clean write after its block's retrieval");
       // the slot it fills held block b-W, last read by block b-1's attention
       if (b > 0)
         for (const Span& a : attn[b - 1]) CHECK(ordered(a, clean[b][l]), "clean write %d after the previous block's attention", b);
-      CHECK(ordered(clean[b][l], upd[b]), "bank update after the block's clean writes");
+      // the update's decision kernel reads only fingerprints; its copies read
+      // the window slot the clean writes fill
+      if (upd[b].end - upd[b].begin > 1)
+        CHECK(ordered(clean[b][l], Span{upd[b].begin + 1, upd[b].end}), "bank copies after the block's clean writes");
     }
     for (const Span& a : attn[b]) CHECK(ordered(a, upd[b]), "bank update %d after the block's attention", b);
     if (b + 1 < n_blocks) CHECK(ordered(Span{upd[b].begin, upd[b].begin + (upd[b].empty() ? 0 : 1)}, retr[b + 1]),
@@ -242,7 +256,8 @@ void stream_checks(int dtype, int window, int bank) {
   int32_t ids[8], misc[3];
   double phi[8 * 558];
   CHECK(pr_sink_bank_state(g.h, ids, phi, misc, A) == PR_SINK_OK, "bank_state");
-  for (const std::string& e : stub::errors()) CHECK(false, "dtype %d window %d bank %d: %s", dtype, window, bank, e.c_str());
+  for (const std::string& e : stub::errors())
+    CHECK(false, "dtype %d window %d bank %d mixed %d: %s", dtype, window, bank, (int)mixed, e.c_str());
 }
 
 }  // namespace
@@ -250,7 +265,8 @@ void stream_checks(int dtype, int window, int bank) {
 int main() {
   dry_run_checks();
   for (int dtype : {PR_SINK_BF16, PR_SINK_F32})
-    for (int w : {1, 2, 3, 5}) stream_checks(dtype, w, w == 5 ? 8 : 5);
+    for (int w : {1, 2, 3, 5})
+      for (bool mixed : {false, true}) stream_checks(dtype, w, w == 5 ? 8 : 5, mixed);
   CHECK(stub::live_events() == 0, "%d HIP events leaked", stub::live_events());
   if (g_failures) {
     std::printf("abi_check: %d failures\n", g_failures);
