@@ -238,16 +238,6 @@ def main():
     rec = counter_record(args.workload)
     if rec is not None:
         result["roofline"]["traffic"] = rec["traffic_bytes_per_launch"]
-        if "shader_clock_ghz" in rec:
-            # the same MFMA peak at the shader clock the counters saw during this kernel
-            peak_clk = PEAK_BF16_TFLOPS * rec["shader_clock_ghz"] / 2.4
-            result["clock_adjusted"] = {
-                "shader_clock_ghz": rec["shader_clock_ghz"],
-                "peak_tflops_at_clock": round(peak_clk, 1),
-                "frac": round(achieved / peak_clk, 4),
-                "mfma_util_pct": rec.get("mfma_util_pct"),
-                "source": f"profiles/attn_bf16_kernel_{args.workload}_traffic.json",
-            }
 
     if not args.no_cpu_baseline:
         import oracle as O

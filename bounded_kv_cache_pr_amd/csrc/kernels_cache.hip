@@ -13,10 +13,13 @@
 namespace prsink {
 namespace {
 
-// Streaming 16-byte accesses (the nt bit): what the clean write and the bank
-// copy read is read once, and what they write is read back only blocks later,
-// so neither should evict from L2 the keys that attention running beside them
-// streams.
+// Streaming 16-byte accesses (the nt bit) in the copies and the clean write:
+// each byte is read or written once per launch, so none of them should evict
+// from L2 the keys that attention running beside them streams; on copies much
+// larger than the L2 they also moved more bytes per second than plain
+// accesses, with one chunk per thread and loop iteration.  (rope_follow keeps
+// plain accesses: the current keys it rotates are read right back by the
+// attention kernel.)
 typedef unsigned int u32x4_nt __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ uint4 ld_nt(const uint4* p) {
   const u32x4_nt v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_nt*>(p));
@@ -39,10 +42,13 @@ __global__ __launch_bounds__(256) void kv_write_kernel(
     size_t n_chunks) {
   const size_t stride = (size_t)gridDim.x * blockDim.x;
   for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n_chunks; i += stride) {
-    const uint4 kv = k_src[i], vv = v_src[i];
-    k_dst0[i] = kv;
-    v_dst0[i] = vv;
-    if (k_dst1) { k_dst1[i] = kv; v_dst1[i] = vv; }
+    const uint4 kv = ld_nt(k_src + i), vv = ld_nt(v_src + i);
+    st_nt(k_dst0 + i, kv);
+    st_nt(v_dst0 + i, vv);
+    if (k_dst1) {
+      st_nt(k_dst1 + i, kv);
+      st_nt(v_dst1 + i, vv);
+    }
   }
 }
 
@@ -61,16 +67,7 @@ __global__ __launch_bounds__(256) void slot_copy_kernel(uint8_t* __restrict__ ba
   uint4* __restrict__ d = reinterpret_cast<uint4*>(base + (size_t)dst * slot_bytes + copy_off);
   const size_t n = copy_bytes / 16;
   const size_t stride = (size_t)gridDim.x * blockDim.x;
-  size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-  for (; i + 3 * stride < n; i += 4 * stride) {
-    const uint4 a = ld_nt(s + i), b = ld_nt(s + i + stride), c = ld_nt(s + i + 2 * stride),
-                e = ld_nt(s + i + 3 * stride);
-    st_nt(d + i, a);
-    st_nt(d + i + stride, b);
-    st_nt(d + i + 2 * stride, c);
-    st_nt(d + i + 3 * stride, e);
-  }
-  for (; i < n; i += stride) st_nt(d + i, ld_nt(s + i));
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) st_nt(d + i, ld_nt(s + i));
 }
 
 // ---------------------------------------------------------------------------
@@ -428,7 +425,7 @@ hipError_t launch_kv_write(const void* k_src, const void* v_src, void* k_dst0, v
                            void* k_dst1, void* v_dst1, size_t bytes, hipStream_t s) {
   const size_t n_chunks = bytes / 16;
   size_t blocks = (n_chunks + 255) / 256;
-  if (blocks > 256 * 8) blocks = 256 * 8;
+  if (blocks > 256 * 32) blocks = 256 * 32;
   hipLaunchKernelGGL(kv_write_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
                      static_cast<const uint4*>(k_src), static_cast<const uint4*>(v_src),
                      static_cast<uint4*>(k_dst0), static_cast<uint4*>(v_dst0),
@@ -449,7 +446,7 @@ hipError_t launch_rope_follow(const RotParams& p, int n_layers, hipStream_t s) {
 hipError_t launch_clean_write(const CleanWrite& p, hipStream_t s) {
   const size_t total = (size_t)p.n_tok * p.n_heads * p.head_dim * p.elem / 16;
   size_t blocks = (total + 255) / 256;
-  if (blocks > 256 * 8) blocks = 256 * 8;
+  if (blocks > 256 * 32) blocks = 256 * 32;
   hipLaunchKernelGGL(clean_write_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p);
   return hipGetLastError();
 }
@@ -458,7 +455,7 @@ hipError_t launch_slot_copy(char* block_base, size_t slot_bytes, size_t copy_off
                             const DevState* st, hipStream_t s) {
   const size_t n16 = copy_bytes / 16;
   size_t blocks = (n16 + 255) / 256;
-  if (blocks > 256 * 16) blocks = 256 * 16;
+  if (blocks > 256 * 128) blocks = 256 * 128;
   hipLaunchKernelGGL(slot_copy_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
                      reinterpret_cast<uint8_t*>(block_base), slot_bytes, copy_off, copy_bytes, st);
   return hipGetLastError();
