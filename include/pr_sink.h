@@ -155,11 +155,18 @@ enum {
 };
 
 /* Bytes of device arena the config needs (0 if the config is invalid).
- * Closed form in the config only: never depends on the stream length. */
+ * The method's cache is bounded: its memory does not grow with the length of
+ * the stream (abstract on the HF papers page; jiazhuangai.com article, its
+ * three key breakthroughs: a fixed memory overhead).  So this is a closed
+ * form in the config only, and the arena is all the device memory the cache
+ * ever uses. */
 size_t pr_sink_arena_bytes(const pr_sink_config* cfg);
 
-/* Creates a cache over `arena_dev` (device memory, >= pr_sink_arena_bytes(cfg)
- * bytes, 256-byte aligned; owned by the caller, must outlive the cache).
+/* Creates the bounded cache of the method (HF papers abstract: sinks plus a
+ * rolling window, in fixed memory; review on paper.rainbus.top, full-pipeline
+ * paragraph: the Ref, Static and Dynamic Sinks and the window slots) over
+ * `arena_dev` (device memory, >= pr_sink_arena_bytes(cfg) bytes, 256-byte
+ * aligned; owned by the caller, must outlive the cache).
  * Clears the arena and uploads the RoPE cos/sin tables, then synchronises
  * `stream`.  With arena_dev == NULL and arena_bytes == 0 it creates a
  * dry-run cache that validates arguments and call order but never touches a
