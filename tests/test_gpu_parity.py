@@ -304,6 +304,9 @@ def _oracle_to(cfg, n_blocks, fps):
 @pytest.mark.parametrize("name,cfg,b,seed", [
     ("C1_480x480", synth.C1_480.replace(n_layers=1), 25, 1),
     ("C2_384x672_slid7", synth.C2_384x672.replace(n_layers=1), 32, 2),
+    # 44 heads: XCDs 0..3 take 6 heads (66 jobs), XCDs 4..7 take 5 (55 jobs),
+    # so the XCDs' job lists differ in length
+    ("C1_44heads_uneven_xcds", synth.C1_480.replace(n_layers=1, n_heads=44), 6, 3),
 ])
 def test_full_size_whole_output_parity(name, cfg, b, seed):
     """Full-size call in the benchmark's launch configuration: every query row of every
