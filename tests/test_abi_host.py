@@ -240,3 +240,49 @@ def test_bench_counter_record_follows_the_kernel_source(tmp_path, monkeypatch):
         assert bench.counter_record("480x480") is None
         (csrc / name).write_bytes(f"// {name}\n".encode())
     assert bench.counter_record("480x480") == rec
+
+
+def test_profile_summary_roles_and_bytes(tmp_path):
+    """profile_summary sorts rocprofv3 dispatches into the path's roles (a rope_follow launch
+    right before attention on its queue rotates the current keys, one right after a
+    slot_copy rotates a bank entry, one before the first retrieval a Ref Sink) and turns
+    DRAM request counts into bytes (x 32)."""
+    import csv
+    from bounded_kv_cache_pr_amd import profile_summary as ps
+    names = {"a": "prsink::attn_bf16_kernel<128>(prsink::AttnParams)",
+             "r": "prsink::rope_follow_kernel(prsink::RotParams)",
+             "k": "prsink::kv_write_kernel(...)", "q": "prsink::retrieve_kernel(...)",
+             "c": "prsink::clean_write_kernel(prsink::CleanWrite)",
+             "u": "prsink::bank_update_kernel(...)", "s": "prsink::slot_copy_kernel(...)"}
+    # (kernel, queue): set-up, then four blocks with the clean path on queue 2
+    seq = [("k", 1), ("r", 1)]
+    for _ in range(4):
+        seq += [("q", 1), ("r", 1), ("a", 1), ("r", 1), ("a", 1), ("c", 2), ("u", 2), ("s", 2), ("r", 2)]
+    d = tmp_path / "dram"
+    d.mkdir()
+    with open(d / "run_counter_collection.csv", "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(["Dispatch_Id", "Queue_Id", "Grid_Size", "Kernel_Name", "Counter_Name", "Counter_Value",
+                    "Start_Timestamp", "End_Timestamp"])
+        t = 0
+        for i, (k, q) in enumerate(seq):
+            for name, val in (("TCC_EA0_RDREQ_DRAM_32B", 100 + i), ("TCC_EA0_WRREQ_WRITE_DRAM_32B", 10)):
+                # counters arrive per hardware instance: two rows that add up
+                w.writerow([i + 1, q, 256, names[k], name, val / 2, t, t + 1000 * (i + 1)])
+                w.writerow([i + 1, q, 256, names[k], name, val / 2, t, t + 1000 * (i + 1)])
+            t += 100000
+    ds = ps.assign_roles(ps.load_pass(str(d)))
+    roles = [x["role"] for x in ds]
+    assert roles[:2] == ["kv_write_kernel", "rope_follow (Ref Sink)"]
+    assert roles[3] == "rope_follow (current keys)" and roles[5] == "rope_follow (current keys)"
+    assert roles[10] == "rope_follow (bank entry)" and roles[19] == "rope_follow (bank entry)"
+    assert roles[7] == "clean_write (block 0, +Static)" and roles[16] == "clean_write"
+    assert [x["block"] for x in ds][:3] == [-1, -1, 0] and ds[11]["block"] == 1
+    assert ds[4]["ctr"]["TCC_EA0_RDREQ_DRAM_32B"] == 104
+    cfg, passes, table, cal = ps.summarise(str(tmp_path), "480x480", 4)
+    assert table["attn_bf16_kernel"]["dram_write"] == 320      # steady dispatches: block 3 on
+    assert table["attn_bf16_kernel"]["n_dram"] == 2
+    # algorithmic bytes of the current-key rotation: T rows + T table rows read, T rows written
+    row = cfg.n_heads * cfg.head_dim * 2
+    assert table["rope_follow (current keys)"]["alg_read"] == cfg.block_tokens * (row + 4 * cfg.head_dim)
+    assert table["attn_bf16_kernel"]["alg_write"] == cfg.block_tokens * row
