@@ -71,11 +71,13 @@ __global__ __launch_bounds__(256) void slot_copy_kernel(uint8_t* __restrict__ ba
 }
 
 // ---------------------------------------------------------------------------
-// rope_follow: RoPE follow for cached keys.  The cache keeps every key raw,
-// and keeps a copy rotated at the positions of each place a block takes: this
-// kernel rotates the Ref Sink at set-up, a bank entry at the Dynamic Sink's
-// place when written, and the current block's keys at the current positions
-// on every call (clean_write rotates the window and Static places) (review on
+// rope_follow: RoPE follow for cached keys.  The cache keeps each block's keys
+// rotated at the positions of every place it takes, computed from the raw
+// keys (kept for the Ref Sink and the window blocks, whose later rotations
+// read them): this kernel rotates the Ref Sink at set-up, a bank entry at the
+// Dynamic Sink's place when written, and the current block's keys at the
+// current positions on every call (clean_write rotates the window and Static
+// places) (review on
 // paper.rainbus.top, full-pipeline paragraph: raw keys re-rotated at their
 // current cache positions; novelty paragraph: position-consistent reuse).
 // Pair (x0, x1) at angle a becomes (x0 cos a - x1 sin a, x0 sin a + x1 cos a),

@@ -285,8 +285,8 @@ struct pr_sink_cache {
 
   char* block_slot(int bs) const { return arena + lay.off_blocks + (size_t)bs * lay.slot_b; }
   char* ref_slot() const { return arena + lay.off_ref; }
-  // raw K, V and rotated K of one layer inside a slot whose tensors are kv bytes
-  // Ref slot: raw K, V and rotated K of layer l
+  // Byte offsets of one layer's tensors inside a slot (tensors of kv_r or kv_b
+  // bytes).  Ref slot: raw K, V and rotated K of layer l
   size_t ref_k(int l) const { return (size_t)l * lay.kv_r; }
   size_t ref_v(int l) const { return ((size_t)cfg.n_layers + l) * lay.kv_r; }
   size_t ref_r(int l) const { return (2 * (size_t)cfg.n_layers + l) * lay.kv_r; }
