@@ -215,7 +215,9 @@ BF16_SMALL = synth.PRSinkConfig(n_layers=2, n_heads=4, head_dim=128, rope_dims=(
     BF16_SMALL.replace(n_heads=9, lat_h=6, lat_w=11, ref_frames=2, block_frames=2, t0=11),
     BF16_SMALL.replace(n_heads=2, lat_h=8, lat_w=8),   # every segment a multiple of 64 keys: no ragged tile
     BF16_SMALL.replace(n_heads=2, lat_h=3, lat_w=5),   # every segment under 64 keys: only ragged tiles
-], ids=["h4d128_q300", "h3d64_q105", "h9d128_ref2_t0", "h2_noragged", "h2_allragged"])
+    # the smallest block: one token per frame, one frame per block and Ref, one head
+    BF16_SMALL.replace(n_heads=1, lat_h=1, lat_w=1, ref_frames=1, block_frames=1),
+], ids=["h4d128_q300", "h3d64_q105", "h9d128_ref2_t0", "h2_noragged", "h2_allragged", "h1_t1"])
 def test_bf16_multitile_every_block(cfg):
     log(f"case: bf16 multi-tile {cfg}")
     st = Stream(cfg, seed=5)
@@ -254,6 +256,24 @@ def test_window_and_bank_sizes(window, bank, dtype):
         st.close(b)
     for i, bid in enumerate(st.orc.bank_ids):
         st.check_slot_bytes(st.cache.slot_index_bank(i), bid, 1)
+
+
+def test_fingerprint_dim_4096():
+    """The largest fingerprint the config allows (4096 dims, against the pages' 558):
+    retrieval slots, bank ids, decisions and fingerprint bits at every block through the
+    fill phase and after it, with recurring poses (swaps) and failed detections (zeros)."""
+    cfg = BF16_SMALL.replace(fp_dim=4096, n_heads=1, lat_h=2, lat_w=2, bank_fill_blocks=14)
+    log("case: fingerprint dim 4096, 20 blocks")
+    rng = np.random.default_rng(17)
+    protos = rng.uniform(0.0, 1.0, size=(6, cfg.fp_dim))
+    st = Stream(cfg, seed=17)
+    for b in range(20):
+        fp = protos[rng.integers(6)] + rng.normal(0.0, 0.05, size=cfg.fp_dim)
+        if rng.uniform() < 0.1:
+            fp[:] = 0.0
+        st.open(b, fp.astype(np.float32))
+        st.attend_check(b % cfg.n_layers, step=0)
+        st.close(b)
 
 
 def test_bank_fill_and_freeze_with_swaps():
