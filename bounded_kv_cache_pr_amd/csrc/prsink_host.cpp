@@ -250,6 +250,7 @@ struct pr_sink_cache {
   int bank_count;     // entries filled so far (the first M blocks are inserted unconditionally)
   bool dyn_present;   // the open block attends the Dynamic Sink
   std::vector<uint8_t> ref_set, written;
+  std::vector<uint8_t> win_raw;  // [window slot][layer]: the slot's raw keys were written
   int n_cu;           // compute units of the device
 
   // Cross-stream order.  Every call may use its own stream; an event marks
@@ -422,6 +423,12 @@ size_t block_bytes(const pr_sink_cache* c, int n_tok) {
 // waited for this recording of m yet (a stream wait is a queue packet that
 // costs microseconds between kernels; the three denoise steps of a layer
 // would otherwise each wait for the same clean write).
+// The bank is written during the fill phase, and later under the CONTINUAL
+// and GATED policies (the device decides whether anything changes).
+bool may_enter_bank(const pr_sink_config& g, int block) {
+  return block < g.bank_fill_blocks || (g.bank_policy & (PR_SINK_BANK_CONTINUAL | PR_SINK_BANK_GATED));
+}
+
 hipError_t after(hipStream_t s, pr_sink_cache::Mark& m) {
   if (!m.set || m.st == s) return hipSuccess;
   if (m.pending) {
@@ -553,6 +560,7 @@ int cache_init(const pr_sink_config* cfg, void* arena_dev, size_t arena_bytes, v
   try {
     c->ref_set.assign(cfg->n_layers, 0);
     c->written.assign(cfg->n_layers, 0);
+    c->win_raw.assign((size_t)cfg->window_slots * cfg->n_layers, 0);
   } catch (...) {
     delete c;
     throw;
@@ -759,7 +767,10 @@ int pr_sink_clean_kv_write(pr_sink_cache* c, int32_t layer, const void* k_raw, c
     // takes from the next block on, newest first (none when the window holds
     // only the current block)
     const int j = b % g.window_slots;
-    cw.dst[0].k = c->window_raw(b % g.window_slots, layer);
+    // raw keys only for a block that may enter the bank: the rotation of a new
+    // bank entry at the Dynamic Sink's place is their only later reader
+    const bool keep_raw = may_enter_bank(g, b);
+    cw.dst[0].k = keep_raw ? c->window_raw(b % g.window_slots, layer) : nullptr;
     cw.dst[0].v = w + c->blk_v(layer);
     for (int p = g.window_slots - 2; p >= 0; --p) {
       CleanDst& d = cw.dst[0];
@@ -786,6 +797,7 @@ int pr_sink_clean_kv_write(pr_sink_cache* c, int32_t layer, const void* k_raw, c
     PRS_HIP(after(s, c->bank));
     PRS_HIP(launch_clean_write(cw, s));
     PRS_HIP(mark(s, c->clean[layer]));
+    c->win_raw[(size_t)j * g.n_layers + layer] = keep_raw;
     const int n_written = (int)std::count(c->written.begin(), c->written.end(), (uint8_t)1);
     if (n_written == 0) {
       c->clean_stream = s;
@@ -811,9 +823,7 @@ int pr_sink_bank_update(pr_sink_cache* c, int32_t block, void* stream) {
     if (!c->written[l]) return fail(PR_SINK_ESTATE, "clean K/V of layer %d not written for block %d", l, block);
   const pr_sink_config& g = c->cfg;
   hipStream_t s = as_stream(stream);
-  // the bank is written during the fill phase, and later under the CONTINUAL
-  // and GATED policies (the device decides whether anything changes)
-  const bool update = block < g.bank_fill_blocks || (g.bank_policy & (PR_SINK_BANK_CONTINUAL | PR_SINK_BANK_GATED));
+  const bool update = may_enter_bank(g, block);
   if (!c->dry) {
     // this block's retrieval (it wrote the fingerprint and the scores the
     // decision reads) and attention (it read bank entries as the Dynamic
@@ -907,7 +917,8 @@ int pr_sink_slot_view(const pr_sink_cache* c, int32_t slot, int32_t layer, void*
   const bool window = slot >= PR_SINK_SLOT_WINDOW0 && slot < PR_SINK_SLOT_WINDOW0 + c->cfg.window_slots;
   char* base = c->block_slot(slot == PR_SINK_SLOT_STATIC ? c->bs_static() : slot - PR_SINK_SLOT_WINDOW0 + 1);
   *t_pad_out = L.tb_pad;
-  *k_dev = window ? c->window_raw(slot - PR_SINK_SLOT_WINDOW0, layer) : nullptr;
+  const int j = slot - PR_SINK_SLOT_WINDOW0;
+  *k_dev = window && c->win_raw[(size_t)j * c->cfg.n_layers + layer] ? c->window_raw(j, layer) : nullptr;
   *v_dev = base + c->blk_v(layer);
   if (k_rot_dev) *k_rot_dev = base + c->blk_r(layer);
   const int W = c->cfg.window_slots;
@@ -915,7 +926,7 @@ int pr_sink_slot_view(const pr_sink_cache* c, int32_t slot, int32_t layer, void*
     // the copy at the place the slot's block holds in the window of the open
     // (else the next) block b: block b-W+d sits at place d-1; d = 0 is the
     // block written in block b, or the one that left the window (newest place)
-    const int j = slot - PR_SINK_SLOT_WINDOW0, b = c->next_block;
+    const int b = c->next_block;
     const int d = ((j - b) % W + W) % W;
     *k_rot_dev = c->window_rot(j, d == 0 ? W - 2 : d - 1, layer);
   }

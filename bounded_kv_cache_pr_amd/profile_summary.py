@@ -139,7 +139,9 @@ def algorithmic_bytes(cfg):
         "rope_follow (current keys)": (T * row + T * tab, T * row),
         "rope_follow (Ref Sink)": (Tr * row + Tr * tab, Tr * row),
         "rope_follow (bank entry)": (L * T * row + T * tab, L * T * row),
-        # K, V in; the window's raw K, V and K rotated at the W-1 window places out
+        # K, V in; raw K (a block that may still enter the bank: every block of
+        # the fill phase, which the profiled runs stay in), V and K rotated at the
+        # W-1 window places out
         "clean_write": (2 * T * row + (W - 1) * T * tab, (2 + W - 1) * T * row),
         "clean_write (block 0, +Static)": (2 * T * row + W * T * tab, (2 + W - 1 + 2) * T * row),
         "slot_copy_kernel": (L * T * row, L * T * row),

@@ -253,14 +253,17 @@ int pr_sink_bank_state(pr_sink_cache* c, int32_t* ids_host, double* fp_host,
 /* Device pointers to the raw K, the V and the rotated K of one slot and
  * layer, for inspection.  All are [t_pad][H][d], token-major like the tensors
  * passed in; t_pad (a multiple of 64; the padding rows are zero) goes to
- * *t_pad_out.  Raw keys are kept for the Ref Sink and the window slots only
- * (the Static Sink and bank entries are attended rotated, and rotated from
- * the window slot's raw keys when written): *k_dev receives NULL for them.  The rotated K holds the keys rotated at the place the slot's
- * block takes in the window of the open block (of the next one between
- * blocks); for the block written in it, or one that has left the window, the
- * newest window place.  Static: at the Static Sink's place; a bank entry: at
- * the Dynamic Sink's place.  k_rot_dev may be NULL.  PR_SINK_SLOT_DYNAMIC is rejected (PR_SINK_EINVAL): view the
- * bank entry the open block retrieved instead. */
+ * *t_pad_out.  Raw keys are kept only where a later rotation reads them: for
+ * the Ref Sink, and for a window slot whose block may still enter the bank
+ * (the fill phase, or the CONTINUAL and GATED policies), whose keys are then
+ * rotated at the Dynamic Sink's place.  The Static Sink and bank entries are
+ * attended rotated only.  *k_dev receives NULL where no raw keys are kept.
+ * The rotated K holds the keys rotated at the place the slot's block takes in
+ * the window of the open block (of the next one between blocks); for the
+ * block written in it, or one that has left the window, the newest window
+ * place.  Static: at the Static Sink's place; a bank entry: at the Dynamic
+ * Sink's place.  k_rot_dev may be NULL.  PR_SINK_SLOT_DYNAMIC is rejected
+ * (PR_SINK_EINVAL): view the bank entry the open block retrieved instead. */
 int pr_sink_slot_view(const pr_sink_cache* c, int32_t slot, int32_t layer, void** k_dev,
                       void** v_dev, void** k_rot_dev, int32_t* t_pad_out);
 

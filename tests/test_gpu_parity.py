@@ -161,17 +161,21 @@ class Stream:
             assert not got[T:].any()
 
     def check_slot_bytes(self, slot, block, layer):
-        """Stored V of a slot (and, in a window slot, its raw K) equal the block's
-        clean K/V bit for bit; padding is zero.  The Static Sink and bank entries
-        keep no raw keys (their rotated keys are checked by check_rotations)."""
+        """Stored V of a slot (and, in a window slot whose block may still enter the
+        bank, its raw K) equal the block's clean K/V bit for bit; padding is zero.
+        The Static Sink and bank entries keep no raw keys (their rotated keys are
+        checked by check_rotations)."""
         kt, vt = self.cache.slot_view(slot, layer)
         k, v = self.clean(block, layer)
-        T = self.cfg.block_tokens
-        W = self.cfg.window_slots
+        c = self.cfg
+        T = c.block_tokens
+        W = c.window_slots
         is_window = binding.SLOT_WINDOW0 <= slot < binding.SLOT_WINDOW0 + W
-        assert (kt is not None) == is_window, f"slot {slot}: raw keys kept only in window slots"
+        may_enter = block < c.bank_fill_blocks or bool(c.bank_policy & 6)
+        assert (kt is not None) == (is_window and may_enter), \
+            f"slot {slot} (block {block}): raw keys kept only for window blocks that may enter the bank"
         bits = torch.int16 if self.dt == torch.bfloat16 else torch.int32
-        pairs = ((kt.cpu(), k), (vt.cpu(), v)) if is_window else ((vt.cpu(), v),)
+        pairs = ((kt.cpu(), k), (vt.cpu(), v)) if kt is not None else ((vt.cpu(), v),)
         for got, src in pairs:
             want = torch.from_numpy(np.ascontiguousarray(src)).to(self.dt)
             assert torch.equal(got[:T].contiguous().view(bits), want.view(bits))
