@@ -238,15 +238,30 @@ def main():
     rec = counter_record(args.workload)
     if rec is not None:
         result["roofline"]["traffic"] = rec["traffic_bytes_per_launch"]
+        if "shader_clock_ghz" in rec:
+            # context, not the fraction of the published peak: the MFMA peak at
+            # the shader clock the counter pass measured during this kernel (a
+            # separate rocprofv3 run; the clock differs from box to box)
+            peak_clk = PEAK_BF16_TFLOPS * rec["shader_clock_ghz"] / 2.4
+            result["clock_adjusted"] = {
+                "shader_clock_ghz": rec["shader_clock_ghz"],
+                "peak_tflops_at_clock": round(peak_clk, 1),
+                "frac": round(achieved / peak_clk, 4),
+                "mfma_busy_pct": rec.get("mfma_util_pct"),
+                "source": f"profiles/attn_bf16_kernel_{args.workload}_traffic.json (counter pass of "
+                          "another run)",
+            }
 
     if not args.no_cpu_baseline:
         import oracle as O
         b = n_blocks
         orc = O.PRSinkOracle(cfg)
         fps_h = fps.cpu().numpy()
+        t_rb = time.perf_counter()
         for blk in range(n_blocks):
             orc.open_block(blk, fps_h[blk])
             orc.close_block(blk)
+        rb_ms = (time.perf_counter() - t_rb) * 1e3 / n_blocks
         orc.open_block(b, fps_h[b])
         host = lambda t: t.float().cpu().numpy()
         l = 0
@@ -255,6 +270,8 @@ def main():
         block_host = lambda bid: tuple(host(x) for x in clean_pool[(bid * L + l) % POOL])
         result["cpu_baseline"] = cpu_baseline(cfg, q, k, v, ref_host, block_host, orc,
                                               args.cpu_budget)
+        # the oracle's retrieval and bank update, per block (the fill phase's blocks)
+        result["cpu_baseline"]["retrieval_bank_ms_per_block"] = round(rb_ms, 3)
     print(json.dumps(result), flush=True)
 
 
