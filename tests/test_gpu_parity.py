@@ -331,6 +331,8 @@ def _oracle_to(cfg, n_blocks, fps):
     # 44 heads: XCDs 0..3 take 6 heads (66 jobs), XCDs 4..7 take 5 (55 jobs),
     # so the XCDs' job lists differ in length
     ("C1_44heads_uneven_xcds", synth.C1_480.replace(n_layers=1, n_heads=44), 6, 3),
+    # the head_dim 64 kernel at full size (the pages' model uses 128)
+    ("C1_d64", synth.C1_480.replace(n_layers=1, head_dim=64, rope_dims=(24, 20, 20)), 6, 4),
 ])
 def test_full_size_whole_output_parity(name, cfg, b, seed):
     """Full-size call in the benchmark's launch configuration: every query row of every
