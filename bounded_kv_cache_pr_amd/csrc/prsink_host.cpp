@@ -792,9 +792,13 @@ int pr_sink_clean_kv_write(pr_sink_cache* c, int32_t layer, const void* k_raw, c
     // Block b-W's bank copy also read the slot: with W >= 2 the retrieval's
     // wait for block b-2's update covers it, with W = 1 it is the last update,
     // so the write also waits for the last update's copies.
+    // It also waits for the previous block's write of this layer (it may be on
+    // another stream): an attention call of this block made after this write
+    // waits on this layer's mark, which must then cover that write too.
     hipStream_t s = as_stream(stream);
     PRS_HIP(after(s, c->retr));
     PRS_HIP(after(s, c->bank));
+    PRS_HIP(after(s, c->clean[layer]));
     PRS_HIP(launch_clean_write(cw, s));
     PRS_HIP(mark(s, c->clean[layer]));
     c->win_raw[(size_t)j * g.n_layers + layer] = keep_raw;

@@ -260,6 +260,55 @@ void stream_checks(int dtype, int window, int bank, bool mixed) {
     CHECK(false, "dtype %d window %d bank %d mixed %d: %s", dtype, window, bank, (int)mixed, e.c_str());
 }
 
+// Attention calls interleaved with the clean writes of their block, over three
+// streams: attention and retrieval on A, bank updates on B, clean writes on A,
+// B or C.  In odd blocks each layer's clean K/V is written before the layer's
+// first attention call, on A, so that call needs no wait for it: the call must
+// still be ordered after the previous block's write of the layer, which went
+// to B or C.
+void interleaved_checks(int dtype, int window, int bank) {
+  stub::reset_log();
+  Rig g(small_config(dtype, window, bank));
+  const pr_sink_config& c = g.c;
+  void* const A = fake_stream(0x3000);
+  void* const B = fake_stream(0x4000);
+  void* const C = fake_stream(0x5000);
+  for (int l = 0; l < c.n_layers; ++l)
+    CHECK(pr_sink_set_ref(g.h, l, g.kr, g.vr, A) == PR_SINK_OK, "set_ref");
+  const int n_blocks = c.bank_fill_blocks + 4;
+  std::vector<std::vector<std::vector<Span>>> attn(n_blocks, std::vector<std::vector<Span>>(c.n_layers));
+  std::vector<std::vector<Span>> clean(n_blocks, std::vector<Span>(c.n_layers));
+  auto attend = [&](int b, int l) {
+    attn[b][l].push_back(logged([&] { CHECK(pr_sink_attend(g.h, l, g.q, g.kc, g.vc, g.out, A) == PR_SINK_OK, "attend"); }));
+  };
+  for (int b = 0; b < n_blocks; ++b) {
+    g.fp[(3 * b) % c.fp_dim] = 1.0f;
+    CHECK(pr_sink_retrieve(g.h, b, g.fp, g.slot, A) == PR_SINK_OK, "retrieve %d", b);
+    for (int l = 0; l < c.n_layers; ++l) {
+      // odd blocks write each layer first, on A; even blocks attend first and
+      // write on C (layer 0) or B
+      const bool write_first = b % 2 == 1;
+      if (!write_first) attend(b, l);
+      clean[b][l] = logged([&] {
+        void* const st = write_first ? A : (l == 0 ? C : B);
+        CHECK(pr_sink_clean_kv_write(g.h, l, g.kc, g.vc, st) == PR_SINK_OK, "clean");
+      });
+      attend(b, l);
+    }
+    CHECK(pr_sink_bank_update(g.h, b, B) == PR_SINK_OK, "bank_update %d", b);
+  }
+  for (int b = 1; b < n_blocks; ++b)
+    for (int l = 0; l < c.n_layers; ++l) {
+      for (const Span& a : attn[b][l])
+        CHECK(ordered(clean[b - 1][l], a), "interleaved: block %d attention of layer %d after the clean write", b, l);
+      for (int l2 = 0; l2 < c.n_layers; ++l2)
+        for (const Span& a : attn[b - 1][l2])
+          CHECK(ordered(a, clean[b][l]), "interleaved: clean write %d after the previous block's attention", b);
+    }
+  for (const std::string& e : stub::errors())
+    CHECK(false, "interleaved dtype %d window %d bank %d: %s", dtype, window, bank, e.c_str());
+}
+
 }  // namespace
 
 int main() {
@@ -267,6 +316,7 @@ int main() {
   for (int dtype : {PR_SINK_BF16, PR_SINK_F32})
     for (int w : {1, 2, 3, 5})
       for (bool mixed : {false, true}) stream_checks(dtype, w, w == 5 ? 8 : 5, mixed);
+  for (int w : {1, 3}) interleaved_checks(PR_SINK_BF16, w, 5);
   CHECK(stub::live_events() == 0, "%d HIP events leaked", stub::live_events());
   if (g_failures) {
     std::printf("abi_check: %d failures\n", g_failures);
