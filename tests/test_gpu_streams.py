@@ -186,14 +186,19 @@ def test_stream_672x384_240_blocks():
     run_stream("672x384", cfg, synth.STREAM_BLOCKS["C4"], fps, seed=4)
 
 
-def _clean_path_stream(cfg, fps, two_streams, full_blocks):
-    """One stream of len(fps) blocks; with two_streams the clean-KV path
-    (clean writes, bank update) runs on a second stream.  Returns the
-    per-call checksums, the full outputs of full_blocks, the bank state and
+def _clean_path_stream(cfg, fps, schedule, full_blocks):
+    """One stream of len(fps) blocks.  schedule "one": every call on one stream;
+    "two": the clean-KV path (clean writes, bank update) on a second stream;
+    "interleaved3": odd blocks write each layer's clean K/V first (on the
+    attention stream) and then attend that layer, even blocks attend a layer
+    and then write it on a third stream (layer 0) or the second one, with the
+    bank update on the second stream.  Returns the per-call checksums keyed by
+    (block, step, layer), the full outputs of full_blocks, the bank state and
     every stored slot."""
     L, S = cfg.n_layers, synth.DENOISE_STEPS
     s1 = torch.cuda.current_stream(DEV)
-    s2 = torch.cuda.Stream(DEV) if two_streams else s1
+    s2 = torch.cuda.Stream(DEV) if schedule != "one" else s1
+    s3 = torch.cuda.Stream(DEV) if schedule == "interleaved3" else s2
     cache = binding.PRSinkCache(cfg, device=DEV)
     for l in range(L):
         cache.set_ref(l, *synth.ref_kv_torch(cfg, l, 6, DEV))
@@ -203,17 +208,33 @@ def _clean_path_stream(cfg, fps, two_streams, full_blocks):
     fps_dev = torch.from_numpy(fps).to(DEV)
     out = torch.empty_like(qkv_pool[0][0])
     w = torch.arange(out.numel(), device=DEV, dtype=torch.int64) % 65521
-    sums, kept = [], {}
+    sums, kept = {}, {}
+
+    def attend(b, s, l):
+        q, k, v = qkv_pool[(b * S * L + s * L + l) % POOL]
+        cache.attend(l, q, k, v, out=out)
+        x = out.view(torch.int16).reshape(-1).to(torch.int64)  # on s1, after the call
+        sums[(b, s, l)] = torch.stack([x.sum(), (x * w).sum()])
+        if b in full_blocks:
+            kept[(b, s, l)] = out.clone()
+
     for b in range(len(fps)):
         cache.retrieve(b, fps_dev[b])
+        if schedule == "interleaved3":
+            for l in range(L):
+                if b % 2:
+                    cache.clean_kv_write(l, *clean_pool[(b * L + l) % POOL])
+                for s in range(S):
+                    attend(b, s, l)
+                if not b % 2:
+                    with torch.cuda.stream(s3 if l == 0 else s2):
+                        cache.clean_kv_write(l, *clean_pool[(b * L + l) % POOL])
+            with torch.cuda.stream(s2):
+                cache.bank_update(b)
+            continue
         for s in range(S):
             for l in range(L):
-                q, k, v = qkv_pool[(b * S * L + s * L + l) % POOL]
-                cache.attend(l, q, k, v, out=out)
-                x = out.view(torch.int16).reshape(-1).to(torch.int64)  # on s1, after the call
-                sums.append(torch.stack([x.sum(), (x * w).sum()]))
-                if b in full_blocks:
-                    kept[(b, s, l)] = out.clone()
+                attend(b, s, l)
         with torch.cuda.stream(s2):
             for l in range(L):
                 cache.clean_kv_write(l, *clean_pool[(b * L + l) % POOL])
@@ -225,11 +246,12 @@ def _clean_path_stream(cfg, fps, two_streams, full_blocks):
             [cache.slot_index_bank(i) for i in range(cfg.bank_size)]:
         for l in range(L):
             slots[(slot, l)] = tuple(None if t is None else t.clone() for t in cache.slot_view(slot, l, rotated=True))
-    return torch.stack(sums).cpu(), kept, (ids, phi, misc), slots
+    keys = sorted(sums)
+    return torch.stack([sums[k] for k in keys]).cpu(), kept, (ids, phi, misc), slots
 
 
-@pytest.mark.parametrize("policy", [0, 7])
-def test_clean_path_on_second_stream_matches_one_stream(policy):
+@pytest.mark.parametrize("policy,schedule", [(0, "two"), (7, "two"), (0, "interleaved3")])
+def test_clean_path_on_second_stream_matches_one_stream(policy, schedule):
     """Clean writes and bank updates on a second stream, ordered by the
     library's events: a clean write waits only for its block's retrieval (it
     overlaps that block's attention), the next block's attention of layer l
@@ -238,7 +260,8 @@ def test_clean_path_on_second_stream_matches_one_stream(policy):
     equals a one-stream run bit for bit, across the bank freeze and the
     window ring; policy 7 (zero fallback, continual writes with K = 3, gated
     refresh) rewrites the bank every block, evicting entries that were
-    retrieved the block before."""
+    retrieved the block before.  The interleaved schedule puts some clean
+    writes before their layer's attention calls, over three streams."""
     cfg = synth.PRSinkConfig(n_layers=4, n_heads=8, head_dim=128, rope_dims=(44, 42, 42),
                              rope_theta=1e4, lat_h=16, lat_w=16, ref_frames=1, block_frames=3)
     if policy:
@@ -249,11 +272,11 @@ def test_clean_path_on_second_stream_matches_one_stream(policy):
         fps[[3, 15, 16]] = 0.0
     else:
         fps = synth.pose_stream(26, n_protos=8, seed=6)
-    log(f"case: clean path on a second stream, bank policy {policy}, 26 blocks, T=768, H=8")
+    log(f"case: clean path on other streams ({schedule}), bank policy {policy}, 26 blocks, T=768, H=8")
     full = {1, 2, 19, 20, 21, 25}
-    a = _clean_path_stream(cfg, fps, False, full)
-    b = _clean_path_stream(cfg, fps, True, full)
-    assert torch.equal(a[0], b[0]), "attention checksums differ between one and two streams"
+    a = _clean_path_stream(cfg, fps, "one", full)
+    b = _clean_path_stream(cfg, fps, schedule, full)
+    assert torch.equal(a[0], b[0]), f"attention checksums differ between one stream and {schedule}"
     for key in a[1]:
         assert torch.equal(a[1][key], b[1][key]), f"output {key} differs"
     for x, y in zip(a[2], b[2]):
