@@ -419,16 +419,16 @@ size_t block_bytes(const pr_sink_cache* c, int n_tok) {
   return (size_t)n_tok * c->cfg.n_heads * c->cfg.head_dim * c->lay.elem;
 }
 
-// Stream s waits for producer m if m ran on another stream and s has not
-// waited for this recording of m yet (a stream wait is a queue packet that
-// costs microseconds between kernels; the three denoise steps of a layer
-// would otherwise each wait for the same clean write).
 // The bank is written during the fill phase, and later under the CONTINUAL
 // and GATED policies (the device decides whether anything changes).
 bool may_enter_bank(const pr_sink_config& g, int block) {
   return block < g.bank_fill_blocks || (g.bank_policy & (PR_SINK_BANK_CONTINUAL | PR_SINK_BANK_GATED));
 }
 
+// Stream s waits for producer m if m ran on another stream and s has not
+// waited for this recording of m yet (a stream wait is a queue packet that
+// costs microseconds between kernels; the three denoise steps of a layer
+// would otherwise each wait for the same clean write).
 hipError_t after(hipStream_t s, pr_sink_cache::Mark& m) {
   if (!m.set || m.st == s) return hipSuccess;
   if (m.pending) {
