@@ -37,7 +37,9 @@ into (t, h, w) bands of adjacent pairs with frequency theta^(-2i/D_band); an
 all-zero fingerprint normalises to zero; argmax ties go to the lowest bank
 slot; "keep the bank unchanged" is one of the replacement options, evaluated
 first, and a swap wins only on a strict decrease; the bank stores the clean
-K/V of the block together with its driving fingerprint.
+K/V of the block together with its driving fingerprint; every squared norm and
+dot product of the fingerprint arithmetic is the plain sum of the rounded
+products in index order (``seq_dot``), which fixes its bits.
 
 Parity unpinned: the RoPE band split / pairing / frequency convention and the
 Ref Sink's temporal slot are this oracle's reading; the pages fix neither.
