@@ -73,21 +73,23 @@ def load_pass(path: str):
     ctr = os.path.join(path, "run_counter_collection.csv")
     rows = {}
     if os.path.exists(trace):
-        for r in csv.DictReader(open(trace)):
-            k = short_name(r["Kernel_Name"])
-            d = int(r["Dispatch_Id"])
-            rows[d] = dict(id=d, kernel=k, name=r["Kernel_Name"], queue=int(r["Queue_Id"]),
-                           grid=int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"]),
-                           start=int(r["Start_Timestamp"]), end=int(r["End_Timestamp"]), ctr={})
+        with open(trace, newline="") as f:
+            for r in csv.DictReader(f):
+                k = short_name(r["Kernel_Name"])
+                d = int(r["Dispatch_Id"])
+                rows[d] = dict(id=d, kernel=k, name=r["Kernel_Name"], queue=int(r["Queue_Id"]),
+                               grid=int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"]),
+                               start=int(r["Start_Timestamp"]), end=int(r["End_Timestamp"]), ctr={})
     elif os.path.exists(ctr):
-        for r in csv.DictReader(open(ctr)):
-            d = int(r["Dispatch_Id"])
-            if d not in rows:
-                rows[d] = dict(id=d, kernel=short_name(r["Kernel_Name"]), name=r["Kernel_Name"],
-                               queue=int(r["Queue_Id"]), grid=int(r["Grid_Size"]),
-                               start=int(r["Start_Timestamp"]), end=int(r["End_Timestamp"]),
-                               ctr=defaultdict(float))
-            rows[d]["ctr"][r["Counter_Name"]] += float(r["Counter_Value"])
+        with open(ctr, newline="") as f:
+            for r in csv.DictReader(f):
+                d = int(r["Dispatch_Id"])
+                if d not in rows:
+                    rows[d] = dict(id=d, kernel=short_name(r["Kernel_Name"]), name=r["Kernel_Name"],
+                                   queue=int(r["Queue_Id"]), grid=int(r["Grid_Size"]),
+                                   start=int(r["Start_Timestamp"]), end=int(r["End_Timestamp"]),
+                                   ctr=defaultdict(float))
+                rows[d]["ctr"][r["Counter_Name"]] += float(r["Counter_Value"])
     else:
         return None
     return [rows[d] for d in sorted(rows)]
